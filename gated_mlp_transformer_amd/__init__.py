@@ -1,0 +1,267 @@
+"""MI355X-native MoE / gated-MLP FFN hot path: Python binding of libmoeffn.so.
+
+Each function has the name of the C entry point it calls (see
+``include/moeffn.h``) and does argument marshalling only: it checks the
+tensors' device, dtype, shape and contiguity, allocates outputs that were not
+passed in (torch supplies device memory), and passes raw pointers and the
+current HIP stream to the library. Every step of the computation runs in the
+library's HIP kernels; nothing here computes, and there is no fallback.
+
+Weights are stored [out_features, in_features]: w_gate / w_up are
+[E, f, d] and w_down is [E, d, f] (the transpose of the pages' W in Y = X W).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional
+
+import torch
+
+from . import _lib
+
+MF_F32, MF_BF16, MF_FP8_E4M3 = 0, 1, 2
+
+_lib.load()  # fail loudly at import if the HIP library is missing
+
+__all__ = [
+    "MoEFFNError", "rmsnorm", "moe_route", "moe_permute_workspace_size", "moe_permute",
+    "grouped_swiglu", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
+    "version",
+]
+
+
+class MoEFFNError(RuntimeError):
+    """A libmoeffn call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        msg = _lib.load().mf_status_string(status).decode()
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def version() -> str:
+    return _lib.load().mf_version().decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MF_BF16
+    if dt == torch.float32:
+        return MF_F32
+    if dt == torch.float8_e4m3fn:
+        return MF_FP8_E4M3
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libmoeffn takes device tensors only")
+        if not t.is_contiguous():
+            raise ValueError("libmoeffn takes contiguous tensors only")
+
+
+def _ok(name: str, status: int) -> None:
+    if status != 0:
+        raise MoEFFNError(name, status)
+
+
+# --------------------------------------------------------------------------
+
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = gamma * x / sqrt(mean(x^2) + eps) over the last dim (bf16 or f32)."""
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(x, gamma, out)
+    if gamma.dtype != x.dtype or out.dtype != x.dtype or x.dim() != 2:
+        raise ValueError("rmsnorm: x [T, d], gamma [d], out [T, d] of one dtype")
+    T, d = x.shape
+    _ok("rmsnorm", _lib.load().rmsnorm(_p(x), _p(gamma), _p(out), T, d, eps,
+                                       _dtype_code(x.dtype), _s(stream)))
+    return out
+
+
+def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8,
+              topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+              stream=None):
+    """Sigmoid-with-bias top-k router: returns (topk_idx [T,k] int32 ascending, topk_w [T,k] f32)."""
+    T, d = x.shape
+    E = w_r.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _dev(x, w_r, bias, topk_idx, topk_w)
+    if x.dtype != torch.bfloat16 or w_r.dtype != torch.bfloat16 or bias.dtype != torch.float32:
+        raise ValueError("moe_route: x, w_r bf16 and bias f32")
+    if w_r.shape[1] != d or bias.shape != (E,):
+        raise ValueError("moe_route: w_r [E, d], bias [E]")
+    _ok("moe_route", _lib.load().moe_route(_p(x), _p(w_r), _p(bias), T, d, E, k, _p(topk_idx),
+                                           _p(topk_w), _s(stream)))
+    return topk_idx, topk_w
+
+
+def moe_permute_workspace_size(T: int, k: int, e_count: int) -> int:
+    return int(_lib.load().moe_permute_workspace_size(T, k, e_count))
+
+
+class PermuteResult(NamedTuple):
+    counts: torch.Tensor     # [e_count] int32
+    offsets: torch.Tensor    # [e_count+1] int32
+    src_token: torch.Tensor  # [T*k] int32 (first offsets[-1] valid)
+    inv_pos: torch.Tensor    # [T, k] int32, -1 = non-local
+    x_perm: Optional[torch.Tensor]  # [T*k, d] (first offsets[-1] rows valid)
+
+
+def moe_permute(topk_idx: torch.Tensor, e_begin: int, e_count: int,
+                x: Optional[torch.Tensor] = None, *, x_perm: Optional[torch.Tensor] = None,
+                counts=None, offsets=None, src_token=None, inv_pos=None, workspace=None,
+                stream=None) -> PermuteResult:
+    """Stable counting sort of routing slots by local expert (+ row gather when x is given)."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    i32 = torch.int32
+    counts = torch.empty(e_count, dtype=i32, device=dev) if counts is None else counts
+    offsets = torch.empty(e_count + 1, dtype=i32, device=dev) if offsets is None else offsets
+    src_token = torch.empty(T * k, dtype=i32, device=dev) if src_token is None else src_token
+    inv_pos = torch.empty((T, k), dtype=i32, device=dev) if inv_pos is None else inv_pos
+    need = moe_permute_workspace_size(T, k, e_count)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    d, xdt = 0, MF_BF16
+    if x is not None:
+        d = x.shape[1]
+        xdt = _dtype_code(x.dtype)
+        if x_perm is None:
+            x_perm = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    _dev(topk_idx, x, x_perm, counts, offsets, src_token, inv_pos, workspace)
+    if topk_idx.dtype != i32:
+        raise ValueError("moe_permute: topk_idx must be int32")
+    _ok("moe_permute", _lib.load().moe_permute(
+        _p(topk_idx), T, k, e_begin, e_count, _p(x), d, xdt, _p(x_perm), _p(counts),
+        _p(offsets), _p(src_token), _p(inv_pos), _p(workspace),
+        workspace.numel() * workspace.element_size(), _s(stream)))
+    return PermuteResult(counts, offsets, src_token, inv_pos, x_perm)
+
+
+def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
+                   w_up: torch.Tensor, w_down: torch.Tensor, s_gate=None, s_up=None,
+                   s_down=None, *, h_work=None, y_perm=None, stream=None):
+    """Grouped expert gated MLPs over expert-contiguous rows. Returns (y_perm, h_work)."""
+    max_rows, d = x_perm.shape
+    e_count, f, d2 = w_gate.shape
+    if d2 != d or w_up.shape != w_gate.shape or tuple(w_down.shape) != (e_count, d, f):
+        raise ValueError("grouped_swiglu: w_gate/w_up [E, f, d], w_down [E, d, f]")
+    if offsets.numel() != e_count + 1 or offsets.dtype != torch.int32:
+        raise ValueError("grouped_swiglu: offsets [E+1] int32")
+    wdt = _dtype_code(w_gate.dtype)
+    if w_up.dtype != w_gate.dtype or w_down.dtype != w_gate.dtype:
+        raise ValueError("grouped_swiglu: one weight dtype")
+    if h_work is None:
+        h_work = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=x_perm.device)
+    _dev(x_perm, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down, h_work, y_perm)
+    _ok("grouped_swiglu", _lib.load().grouped_swiglu(
+        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate), _p(w_up), _p(w_down), wdt,
+        _p(s_gate), _p(s_up), _p(s_down), _p(h_work), _p(y_perm), _s(stream)))
+    return y_perm, h_work
+
+
+def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor,
+                out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """out[t] = sum_j topk_w[t,j] * y_perm[inv_pos[t,j]] over local slots."""
+    T, k = inv_pos.shape
+    max_rows, d = y_perm.shape
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=y_perm.device)
+    _dev(y_perm, inv_pos, topk_w, out)
+    _ok("moe_combine", _lib.load().moe_combine(_p(y_perm), _p(inv_pos), _p(topk_w), T, k, d,
+                                               max_rows, _p(out), _dtype_code(out.dtype),
+                                               _s(stream)))
+    return out
+
+
+def tp_shard_mlp(x: torch.Tensor, w_gate_s: torch.Tensor, w_up_s: torch.Tensor,
+                 w_down_s: torch.Tensor, *, h_work=None, partial=None, stream=None):
+    """One TP shard of the dense gated MLP. Returns (partial f32 [T,d], h_work [T,f_s])."""
+    T, d = x.shape
+    fs = w_gate_s.shape[0]
+    if (tuple(w_gate_s.shape) != (fs, d) or tuple(w_up_s.shape) != (fs, d)
+            or tuple(w_down_s.shape) != (d, fs)):
+        raise ValueError("tp_shard_mlp: w_gate_s/w_up_s [f_s, d], w_down_s [d, f_s]")
+    if h_work is None:
+        h_work = torch.empty((T, fs), dtype=x.dtype, device=x.device)
+    if partial is None:
+        partial = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _dev(x, w_gate_s, w_up_s, w_down_s, h_work, partial)
+    _ok("tp_shard_mlp", _lib.load().tp_shard_mlp(
+        _p(x), _p(w_gate_s), _p(w_up_s), _p(w_down_s), T, d, fs, _dtype_code(x.dtype),
+        _p(h_work), _p(partial), _s(stream)))
+    return partial, h_work
+
+
+# --------------------------------------------------------------------------
+
+
+class MoEFFNLayer:
+    """One rank's MoE FFN sub-block, FFN(RMSNorm(x)), with buffers allocated once.
+
+    ``forward`` enqueues rmsnorm -> moe_route -> moe_permute -> grouped_swiglu ->
+    moe_combine on the current stream and returns the [T, d] bf16 output (the
+    partial sum over this rank's experts [e_begin, e_begin + e_count)).
+    """
+
+    def __init__(self, *, T: int, d: int, f: int, w_r, bias, w_gate, w_up, w_down,
+                 e_begin: int = 0, gamma=None, s_gate=None, s_up=None, s_down=None,
+                 k: int = 8, eps: float = 1e-5, out_dtype=torch.bfloat16):
+        dev = w_r.device
+        self.T, self.d, self.f, self.k, self.eps = T, d, f, k, eps
+        self.e_begin, self.e_count = e_begin, w_gate.shape[0]
+        self.gamma, self.w_r, self.bias = gamma, w_r, bias
+        self.w = (w_gate, w_up, w_down)
+        self.s = (s_gate, s_up, s_down)
+        bf = torch.bfloat16
+        rows = T * k
+        self.v = torch.empty((T, d), dtype=bf, device=dev) if gamma is not None else None
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(self.e_count, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(self.e_count + 1, dtype=torch.int32, device=dev)
+        self.src_token = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.inv_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.workspace = torch.empty(max(1, moe_permute_workspace_size(T, k, self.e_count)),
+                                     dtype=torch.uint8, device=dev)
+        self.x_perm = torch.empty((rows, d), dtype=bf, device=dev)
+        self.h = torch.empty((rows, f), dtype=bf, device=dev)
+        self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
+        self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
+
+    def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+        v = x
+        if self.gamma is not None:
+            v = rmsnorm(x, self.gamma, self.eps, out=self.v, stream=stream)
+        moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, stream=stream)
+        moe_permute(self.idx, self.e_begin, self.e_count, v, x_perm=self.x_perm,
+                    counts=self.counts, offsets=self.offsets, src_token=self.src_token,
+                    inv_pos=self.inv_pos, workspace=self.workspace, stream=stream)
+        grouped_swiglu(self.x_perm, self.offsets, *self.w, *self.s, h_work=self.h,
+                       y_perm=self.y_perm, stream=stream)
+        return moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out, stream=stream)
+
+    __call__ = forward

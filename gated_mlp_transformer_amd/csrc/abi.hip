@@ -1,0 +1,171 @@
+// C ABI of the FFN hot path: argument validation, then kernel launches on the
+// caller's stream. Nothing here allocates, synchronises or keeps state.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "moeffn.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647LL;
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+int finish() { return hipGetLastError() == hipSuccess ? MF_OK : MF_EHIP; }
+
+hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mf_version(void) { return "moeffn 0.1.0 (gfx950)"; }
+
+const char* mf_status_string(int status) {
+  switch (status) {
+    case MF_OK: return "MF_OK";
+    case MF_EINVAL: return "MF_EINVAL: invalid argument";
+    case MF_EUNSUPPORTED: return "MF_EUNSUPPORTED: valid arguments outside what the kernels implement";
+    case MF_EHIP: return "MF_EHIP: HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d, float eps,
+            int32_t dtype, void* stream) {
+  if (T < 0 || d <= 0 || !(eps >= 0.f) || !isfinite(eps)) return MF_EINVAL;
+  if (dtype != MF_BF16 && dtype != MF_F32) return MF_EINVAL;
+  if (d % 64 != 0 || d > (dtype == MF_BF16 ? 8192 : 4096)) return MF_EUNSUPPORTED;
+  if (T == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!x || !gamma || !y) return MF_EINVAL;
+  if (!a16(x) || !a16(gamma) || !a16(y)) return MF_EUNSUPPORTED;
+  if ((T + 3) / 4 > 0xFFFFFFFFLL) return MF_EUNSUPPORTED;
+  mf::launch_rmsnorm(x, gamma, y, T, d, eps, dtype == MF_BF16, S(stream));
+  return finish();
+}
+
+int moe_route(const void* x, const void* w_r, const float* bias, int64_t T, int32_t d, int32_t E,
+              int32_t k, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (!w_r || !bias || T < 0 || d <= 0) return MF_EINVAL;
+  if (k <= 0 || E < k) return MF_EINVAL;
+  if (k != 8 || E > 256 || d % 64 != 0) return MF_EUNSUPPORTED;
+  if (T > kI32Max / 8) return MF_EUNSUPPORTED;
+  if (T == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!x || !topk_idx || !topk_w) return MF_EINVAL;
+  if (!a16(x) || !a16(w_r)) return MF_EUNSUPPORTED;
+  mf::launch_route(x, w_r, bias, T, d, E, topk_idx, topk_w, S(stream));
+  return finish();
+}
+
+size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t e_count) {
+  if (T < 0 || k < 1 || k > 8 || e_count < 1 || e_count > 256 || T > kI32Max / 8) return 0;
+  return mf::permute_workspace_bytes(T, e_count);
+}
+
+int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin, int32_t e_count,
+                const void* x, int32_t d, int32_t x_dtype, void* x_perm, int32_t* counts,
+                int32_t* offsets, int32_t* src_token, int32_t* inv_pos, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!counts || !offsets || !workspace) return MF_EINVAL;
+  if (T < 0 || k < 1 || e_begin < 0 || e_count < 1) return MF_EINVAL;
+  if (T > 0 && (!topk_idx || !src_token || !inv_pos)) return MF_EINVAL;  // NULL only if empty
+  if (k > 8 || e_count > 256 || T > kI32Max / 8) return MF_EUNSUPPORTED;
+  if (workspace_bytes < mf::permute_workspace_bytes(T, e_count)) return MF_EINVAL;
+  if (!a16(workspace)) return MF_EUNSUPPORTED;
+  int64_t row_bytes = 0;
+  if (x != nullptr && T > 0) {
+    if (!x_perm || d <= 0) return MF_EINVAL;
+    if (x_dtype != MF_BF16 && x_dtype != MF_F32) return MF_EINVAL;
+    row_bytes = static_cast<int64_t>(d) * (x_dtype == MF_BF16 ? 2 : 4);
+    if (row_bytes % 16 != 0 || !a16(x) || !a16(x_perm)) return MF_EUNSUPPORTED;
+  }
+  mf::launch_permute(topk_idx, T, k, e_begin, e_count, T > 0 ? x : nullptr, row_bytes, x_perm,
+                     counts, offsets,
+                     src_token, inv_pos, workspace, S(stream));
+  return finish();
+}
+
+int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count, int64_t max_rows,
+                   int32_t d, int32_t f, const void* w_gate, const void* w_up, const void* w_down,
+                   int32_t w_dtype, const float* s_gate, const float* s_up, const float* s_down,
+                   void* h_work, void* y_perm, void* stream) {
+  if (!offsets || !w_gate || !w_up || !w_down) return MF_EINVAL;
+  if (e_count < 1 || max_rows < 0 || d <= 0 || f <= 0) return MF_EINVAL;
+  if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
+  if (w_dtype == MF_FP8_E4M3 && (!s_gate || !s_up || !s_down)) return MF_EINVAL;
+  if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 128 != 0)) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_FP8_E4M3 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
+  if (max_rows == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!x_perm || !h_work || !y_perm) return MF_EINVAL;
+  if (!a16(x_perm) || !a16(w_gate) || !a16(w_up) || !a16(w_down) || !a16(h_work) || !a16(y_perm))
+    return MF_EUNSUPPORTED;
+  const hipStream_t s = S(stream);
+  if (w_dtype == MF_BF16) {
+    const int cus = num_cus();
+    mf::launch_gemm_gateup_bf16(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, h_work,
+                                cus, s);
+    mf::launch_gemm_down_bf16(h_work, offsets, e_count, max_rows, f, d, w_down, y_perm, false,
+                              cus, s);
+  } else {
+    mf::launch_gemm_gateup_fp8(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
+                               s_up, h_work, s);
+    mf::launch_gemm_down_fp8(h_work, offsets, e_count, max_rows, f, d, w_down, s_down, y_perm, s);
+  }
+  return finish();
+}
+
+int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w, int64_t T,
+                int32_t k, int32_t d, int64_t max_rows, void* out, int32_t out_dtype,
+                void* stream) {
+  if (T < 0 || k < 1 || d <= 0 || max_rows < 0) return MF_EINVAL;
+  if (out_dtype != MF_BF16 && out_dtype != MF_F32) return MF_EINVAL;
+  if (k > 8 || d % 64 != 0 || T > 0xFFFFFFFFLL) return MF_EUNSUPPORTED;
+  if (T == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!inv_pos || !topk_w || !out || (!y_perm && max_rows > 0)) return MF_EINVAL;
+  if (!a16(y_perm) || !a16(out)) return MF_EUNSUPPORTED;
+  mf::launch_combine(y_perm, inv_pos, topk_w, T, k, d, max_rows, out, out_dtype == MF_F32,
+                     S(stream));
+  return finish();
+}
+
+int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s, const void* w_down_s,
+                 int64_t T, int32_t d, int32_t f_s, int32_t dtype, void* h_work, float* partial,
+                 void* stream) {
+  if (!w_gate_s || !w_up_s || !w_down_s) return MF_EINVAL;
+  if (T < 0 || d <= 0 || f_s <= 0) return MF_EINVAL;
+  if (dtype != MF_BF16 && dtype != MF_F32) return MF_EINVAL;
+  if (T > kI32Max) return MF_EUNSUPPORTED;
+  if (T > 0 && (!x || !h_work || !partial)) return MF_EINVAL;  // NULL only if empty
+  if (dtype == MF_BF16) {
+    if (d % 256 != 0 || f_s % 128 != 0) return MF_EUNSUPPORTED;
+    if (!a16(x) || !a16(w_gate_s) || !a16(w_up_s) || !a16(w_down_s) || !a16(h_work) ||
+        !a16(partial))
+      return MF_EUNSUPPORTED;
+  } else if ((T + 15) / 16 > 65535) {
+    return MF_EUNSUPPORTED;
+  }
+  if (T == 0) return MF_OK;
+  const hipStream_t s = S(stream);
+  if (dtype == MF_BF16) {
+    const int cus = num_cus();
+    mf::launch_gemm_gateup_bf16(x, nullptr, 1, T, d, f_s, w_gate_s, w_up_s, h_work, cus, s);
+    mf::launch_gemm_down_bf16(h_work, nullptr, 1, T, f_s, d, w_down_s, partial, true, cus, s);
+  } else {
+    mf::launch_dense_f32(static_cast<const float*>(x), static_cast<const float*>(w_gate_s),
+                         static_cast<const float*>(w_up_s), static_cast<const float*>(w_down_s),
+                         T, d, f_s, static_cast<float*>(h_work), partial, s);
+  }
+  return finish();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Weighted un-permute ("推理计算流梳理", EP 路径: expert outputs summed with the
+// router weights back at the token's source; "「赤兔」Chitu ... MoE":
+// token_unpermutation):
+//   out[t] = sum_{j : inv_pos[t,j] valid} w[t,j] * y_perm[inv_pos[t,j]].
+//
+// A gather, not a scatter: one 256-thread workgroup per token reads at most k
+// rows of y_perm with 16-byte loads and sums them in fp32 in slot order, so the
+// result is deterministic and needs no atomics. HBM-bound: the bytes are the k
+// rows read plus the output row written.
+#include "common.h"
+#include "launch.h"
+
+namespace mf {
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ inv_pos,
+                                                      const float* __restrict__ w, int k, int d,
+                                                      int64_t max_rows, void* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  int64_t pos[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pos[j] = -1;
+    wt[j] = 0.f;
+    if (j < k) {
+      const int64_t p = inv_pos[t * k + j];
+      if (p >= 0 && p < max_rows) {
+        pos[j] = p;
+        wt[j] = w[t * k + j];
+      }
+    }
+  }
+  const int nvec = d / 8;
+  for (int v = threadIdx.x; v < nvec; v += 256) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    u32x4 rows[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (pos[j] >= 0) rows[j] = ld16(y + pos[j] * d + static_cast<int64_t>(v) * 8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (pos[j] >= 0) {
+        float f[8];
+        unpack_bf16x8(rows[j], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[j], f[e], acc[e]);
+      }
+    }
+    if constexpr (OUT_F32) {
+      float* o = static_cast<float*>(out) + t * d + static_cast<int64_t>(v) * 8;
+      st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                    __float_as_uint(acc[3])});
+      st16(o + 4, u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                        __float_as_uint(acc[6]), __float_as_uint(acc[7])});
+    } else {
+      bf16_t* o = static_cast<bf16_t*>(out) + t * d + static_cast<int64_t>(v) * 8;
+      st16(o, pack_bf16x8(acc));
+    }
+  }
+}
+
+void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w, int64_t T, int k,
+                    int d, int64_t max_rows, void* out, bool out_f32, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(T));
+  if (out_f32)
+    combine_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(y_perm), inv_pos, w, k,
+                                              d, max_rows, out);
+  else
+    combine_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(y_perm), inv_pos, w, k,
+                                               d, max_rows, out);
+}
+
+}  // namespace mf

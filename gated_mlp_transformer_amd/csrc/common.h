@@ -1,0 +1,102 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16/fp8
+// conversions, MFMA wrappers, wave reductions and launch-time constants.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mf {
+
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+// ---- conversions --------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// Two fp32 -> packed bf16x2 (low half = a), round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Unpack 8 bf16 held in a 16-byte vector into fp32.
+__device__ __forceinline__ void unpack_bf16x8(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return r;
+}
+
+// Four E4M3FN codes (one dword) -> four bf16 (two dwords), exactly: every
+// E4M3FN value, subnormals included, is representable in bf16. Uses the
+// gfx950 conversion with a unit scale.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t q) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, true);
+  u32x2 r;
+  r[0] = __builtin_bit_cast(uint32_t, lo);
+  r[1] = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// ---- MFMA ---------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].
+// Lane l supplies A[l%16][8*(l/16)+v] and B[8*(l/16)+v][l%16] (v = 0..7) and
+// holds D[4*(l/16)+r][l%16] (r = 0..3).
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- wave reductions ----------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// ---- math ----------------------------------------------------------------
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float siluf_(float a) { return a / (1.0f + expf(-a)); }
+
+// ---- global memory -------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+}  // namespace mf

@@ -1,0 +1,49 @@
+// Internal launchers: one per kernel family. Arguments are validated by the
+// C-ABI layer (abi.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mf {
+
+void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
+                    float eps, bool bf16, hipStream_t s);
+
+void launch_route(const void* x, const void* w_r, const float* bias, int64_t T,
+                  int d, int E, int32_t* idx, float* w, hipStream_t s);
+
+size_t permute_workspace_bytes(int64_t T, int e_count);
+void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_count,
+                    const void* x, int64_t row_bytes, void* x_perm, int32_t* counts,
+                    int32_t* offsets, int32_t* src_token, int32_t* inv_pos,
+                    void* workspace, hipStream_t s);
+
+// bf16 MFMA grouped GEMMs. offsets == nullptr means one group of max_rows rows.
+void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
+                             int64_t max_rows, int K, int N, const void* w_gate,
+                             const void* w_up, void* h, int num_cus, hipStream_t s);
+void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count,
+                           int64_t max_rows, int K, int N, const void* w_down,
+                           void* y, bool out_f32, int num_cus, hipStream_t s);
+
+// fp8-weight (block-scaled) grouped GEMMs.
+void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count,
+                            int64_t max_rows, int K, int N, const void* w_gate,
+                            const void* w_up, const float* s_gate, const float* s_up,
+                            void* h, hipStream_t s);
+void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
+                          int64_t max_rows, int K, int N, const void* w_down,
+                          const float* s_down, void* y, hipStream_t s);
+
+void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w,
+                    int64_t T, int k, int d, int64_t max_rows, void* out,
+                    bool out_f32, hipStream_t s);
+
+// fp32 dense shard (FMA, no MFMA).
+void launch_dense_f32(const float* x, const float* w_gate, const float* w_up,
+                      const float* w_down, int64_t T, int d, int fs, float* h,
+                      float* partial, hipStream_t s);
+
+}  // namespace mf

@@ -1,0 +1,203 @@
+/*
+ * moeffn.h - C ABI of the MI355X (gfx950) MoE / gated-MLP FFN hot path.
+ *
+ * One GPU's share of a Pre-Norm transformer FFN sub-block, FFN(RMSNorm(R)),
+ * as pages on LLM inference describe it ("推理计算流梳理", Norm&Residual,
+ * 实际 MLP 计算策略, 专家并行; "「赤兔」Chitu 框架深度解读（七）：MoE", token
+ * dispatchers and experts):
+ *
+ *   rmsnorm -> moe_route -> moe_permute -> grouped_swiglu -> moe_combine
+ *
+ * plus the dense tensor-parallel shard of the same gated MLP, tp_shard_mlp.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor argument is caller-owned DEVICE memory on the current HIP
+ *    device, row-major and contiguous, 16-byte aligned. Sizes are in elements.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *    the null stream). They never synchronise the host, never allocate device
+ *    memory and keep no mutable global state, so they are re-entrant. Calls
+ *    that share an output or workspace buffer must be ordered by the caller.
+ *  - Linear-layer weights are stored [out_features, in_features] (each output
+ *    feature's weights contiguous), i.e. the transpose of the pages' W in
+ *    Y = X W. The router weight W_r is [E, d], as in the pages' z = x W_r^T.
+ *  - Return value: MF_OK (0), MF_EINVAL (-1: null pointer, bad size or value),
+ *    MF_EUNSUPPORTED (-2: valid but outside what the kernels implement, such
+ *    as a dtype combination, an alignment or a dimension that is not a
+ *    multiple of the tile), MF_EHIP (-3: the HIP runtime reported an error at
+ *    launch). Arguments are validated before anything is enqueued: on
+ *    MF_EINVAL or MF_EUNSUPPORTED nothing was enqueued.
+ *  - A call with zero tokens/rows is valid; it enqueues only what is needed
+ *    to leave the outputs well defined (moe_permute still writes zero counts
+ *    and offsets) and returns MF_OK.
+ *  - Data-dependent values (token ids, expert ids, offsets, row indices) are
+ *    clamped or skipped by the kernels so that no access leaves its buffer,
+ *    whatever the device data holds.
+ */
+#ifndef MOEFFN_H
+#define MOEFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MF_OK = 0, MF_EINVAL = -1, MF_EUNSUPPORTED = -2, MF_EHIP = -3 };
+enum { MF_F32 = 0, MF_BF16 = 1, MF_FP8_E4M3 = 2 };
+
+/* Human-readable name of a status code (static storage). */
+const char* mf_status_string(int status);
+
+/* Library version string (static storage). */
+const char* mf_version(void);
+
+/*
+ * rmsnorm - y[t, j] = gamma[j] * x[t, j] / sqrt(mean_k x[t, k]^2 + eps).
+ *
+ * "推理计算流梳理", Norm&Residual: the RMSNorm equation (the mean square over
+ * the hidden vector, eps = 1e-5 inside the square root) and V = RMSNorm_ffn(R),
+ * the input of the FFN.
+ *
+ * x, y   [T, d]  dtype (MF_BF16 or MF_F32); y may alias x.
+ * gamma  [d]     dtype.
+ * Math in fp32; y is rounded to nearest-even into dtype.
+ * Requires d % 64 == 0 and d <= 8192 (bf16) / d <= 4096 (f32); eps >= 0.
+ */
+int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
+            float eps, int32_t dtype, void* stream);
+
+/*
+ * moe_route - sigmoid-with-bias top-k expert router.
+ *
+ * "推理计算流梳理", 专家并行 / MoE Router 过程, router equation:
+ *   z = x W_r^T,  s = sigmoid(z),  I = Top8(s + b),  w_i = s_i / sum_{j in I} s_j.
+ * The bias only selects experts; the weights use the unbiased scores.
+ *
+ * x        [T, d] bf16      router input (RMSNorm output inside the FFN block)
+ * w_r      [E, d] bf16      router weight
+ * bias     [E]    f32
+ * topk_idx [T, k] int32     out: the k selected expert ids of each token, in
+ *                           ascending order (I is a set)
+ * topk_w   [T, k] f32       out: w_i aligned with topk_idx; each row sums to 1
+ * Logits are bf16 x bf16 products accumulated in fp32 (MFMA); s, s + b and
+ * w are fp32. Ties in s + b go to the lower expert id.
+ * Requires k == 8, 8 <= E <= 256, d % 64 == 0.
+ */
+int moe_route(const void* x, const void* w_r, const float* bias, int64_t T,
+              int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/*
+ * moe_permute_workspace_size - bytes of device workspace moe_permute needs.
+ * Returns 0 for invalid arguments (then moe_permute would return MF_EINVAL).
+ */
+size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t e_count);
+
+/*
+ * moe_permute - stable counting sort of the routing slots (t, j) by expert,
+ * over the local experts [e_begin, e_begin + e_count), and the gather of the
+ * token rows into that expert-contiguous order.
+ *
+ * "「赤兔」Chitu 框架深度解读（七）：MoE": token_permutation of a dispatcher with
+ * no communication, and the expert-contiguous token layout its grouped GEMM
+ * consumes; "推理计算流梳理", EP 路径: each rank runs its own experts.
+ *
+ * topk_idx  [T, k] int32   expert ids; ids in a row must be distinct (the
+ *                          router's always are); ids outside the local range
+ *                          are dropped
+ * x         [T, d] or NULL rows to gather (x_dtype MF_BF16 or MF_F32); NULL
+ *                          computes the indices only and leaves x_perm untouched
+ * x_perm    [T*k, d]       out: row r = x[src_token[r]] for r < offsets[e_count]
+ * counts    [e_count] i32  out: slots per local expert
+ * offsets   [e_count+1]    out: exclusive prefix sum of counts, offsets[0] = 0
+ * src_token [T*k] i32      out: token of each permuted row (first
+ *                          offsets[e_count] entries); tokens ascend within an
+ *                          expert (stable)
+ * inv_pos   [T, k] i32     out: permuted row of slot (t, j), -1 if non-local
+ * workspace                moe_permute_workspace_size(T, k, e_count) bytes
+ * Integer results are exact and deterministic (no order-dependent atomics).
+ * Requires k == 8, 1 <= e_count <= 256, e_begin >= 0, T*k < 2^31, and
+ * (when x != NULL) d * sizeof(x_dtype) % 16 == 0.
+ */
+int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
+                int32_t e_count, const void* x, int32_t d, int32_t x_dtype,
+                void* x_perm, int32_t* counts, int32_t* offsets,
+                int32_t* src_token, int32_t* inv_pos, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * grouped_swiglu - every local expert's gated MLP over its contiguous rows:
+ *   H[o_e:o_{e+1}]      = SiLU(X_perm W_gate_e) * (X_perm W_up_e)
+ *   Y_perm[o_e:o_{e+1}] = H[o_e:o_{e+1}] W_down_e
+ *
+ * "推理计算流梳理", 实际 MLP 计算策略 (the gated MLP equation) and EP 路径 (one
+ * rank runs many experts as one grouped GEMM); "「赤兔」Chitu ... MoE", experts
+ * (BatchedExperts; one kernel for all experts; block-fp8 quantised experts).
+ *
+ * x_perm   [max_rows, d] bf16    rows grouped by expert (moe_permute output)
+ * offsets  [e_count+1] int32     device; expert e owns rows [offsets[e], offsets[e+1])
+ * w_gate, w_up [e_count, f, d]   w_dtype (MF_BF16, or MF_FP8_E4M3 codes)
+ * w_down   [e_count, d, f]       w_dtype
+ * s_gate, s_up [e_count, f/128, d/128] f32, s_down [e_count, d/128, f/128] f32:
+ *                                fp8 only (NULL for bf16): one scale per 128x128
+ *                                block; weight value = code value * scale
+ * h_work   [max_rows, f] bf16    out: H (the bf16 operand of the down GEMM)
+ * y_perm   [max_rows, d] bf16    out: expert outputs (rows < offsets[e_count])
+ * max_rows bounds the rows (T*k after moe_permute), so no host sync is needed.
+ * GEMMs run on MFMA with bf16 operands and fp32 accumulation; SiLU(g)*u is
+ * fused into the gate/up epilogue in fp32. fp8 codes are converted to bf16
+ * exactly and each 128-deep partial sum is scaled in fp32.
+ * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 128 == 0;
+ * fp8: d % 256 == 0 and f % 256 == 0.
+ */
+int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count,
+                   int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
+                   const void* w_up, const void* w_down, int32_t w_dtype,
+                   const float* s_gate, const float* s_up, const float* s_down,
+                   void* h_work, void* y_perm, void* stream);
+
+/*
+ * moe_combine - out[t] = sum_{j : inv_pos[t,j] >= 0} topk_w[t,j] * y_perm[inv_pos[t,j]].
+ *
+ * "推理计算流梳理", EP 路径: the expert outputs are summed with the router
+ * weights back at the token's source ("「赤兔」Chitu ... MoE":
+ * token_unpermutation). The global weights are used as they are (no
+ * renormalisation over local experts): a token with no local expert gets 0,
+ * and the outputs of disjoint expert ranges add up to the full FFN output.
+ *
+ * y_perm  [max_rows, d] bf16; inv_pos [T, k] int32 (entries < 0 or >= max_rows
+ * are skipped); topk_w [T, k] f32; out [T, d] out_dtype (MF_BF16 or MF_F32).
+ * fp32 accumulation in slot order j = 0..k-1. Requires 1 <= k <= 8, d % 64 == 0.
+ */
+int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
+                int64_t T, int32_t k, int32_t d, int64_t max_rows, void* out,
+                int32_t out_dtype, void* stream);
+
+/*
+ * tp_shard_mlp - one tensor-parallel shard of the dense gated MLP:
+ *   H_i = SiLU(X W_gate[:, F_i]) * (X W_up[:, F_i]),   P_i = H_i W_down[F_i, :]
+ *
+ * "推理计算流梳理", 实际 MLP 计算策略 (W_gate / W_up column-parallel, the pointwise
+ * part needs no communication, W_down row-parallel) and 行并行 (each rank's
+ * output has the full shape but is only part of the sum); "tensor_parallelism",
+ * Outer Dim / Inner Dim; "LLM推理并行优化的必备知识" §1.4.
+ *
+ * x        [T, d]    dtype
+ * w_gate_s, w_up_s [f_s, d] dtype: rows F_i of the [f, d] storage
+ * w_down_s [d, f_s]  dtype: columns F_i of the [d, f] storage, contiguous
+ * h_work   [T, f_s]  dtype, out: H_i
+ * partial  [T, d]    f32, out: P_i, the full-shape partial sum
+ * dtype MF_BF16 (MFMA, fp32 accumulation; H_i rounded to bf16; requires
+ * d % 256 == 0, f_s % 128 == 0) or MF_F32 (fp32 FMA throughout; any sizes).
+ */
+int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s,
+                 const void* w_down_s, int64_t T, int32_t d, int32_t f_s,
+                 int32_t dtype, void* h_work, float* partial, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEFFN_H */
