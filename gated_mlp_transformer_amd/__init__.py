@@ -26,7 +26,7 @@ _lib.load()  # fail loudly at import if the HIP library is missing
 
 __all__ = [
     "MoEFFNError", "rmsnorm", "moe_route", "moe_permute_workspace_size", "moe_permute",
-    "grouped_swiglu", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
+    "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
     "version",
 ]
 
@@ -182,6 +182,46 @@ def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Te
     return y_perm, h_work
 
 
+def _grouped_dtype(w_gate, *rest):
+    wdt = _dtype_code(w_gate.dtype)
+    if any(w.dtype != w_gate.dtype for w in rest):
+        raise ValueError("grouped GEMM: one weight dtype")
+    if wdt == MF_F32:
+        raise ValueError("grouped GEMM: weights are bf16 or float8_e4m3fn")
+    return wdt
+
+
+def grouped_gate_up(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
+                    w_up: torch.Tensor, s_gate=None, s_up=None, *, h_out=None,
+                    stream=None) -> torch.Tensor:
+    """H = SiLU(X_perm W_gate_e) * (X_perm W_up_e) per expert segment. Returns h_out."""
+    max_rows, d = x_perm.shape
+    e_count, f, _ = w_gate.shape
+    wdt = _grouped_dtype(w_gate, w_up)
+    if h_out is None:
+        h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
+    _dev(x_perm, offsets, w_gate, w_up, s_gate, s_up, h_out)
+    _ok("grouped_gate_up", _lib.load().grouped_gate_up(
+        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate), _p(w_up), wdt,
+        _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
+    return h_out
+
+
+def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s_down=None, *,
+                 y_perm=None, stream=None) -> torch.Tensor:
+    """Y_perm = H W_down_e per expert segment. Returns y_perm."""
+    max_rows, f = h.shape
+    e_count, d, _ = w_down.shape
+    wdt = _grouped_dtype(w_down)
+    if y_perm is None:
+        y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=h.device)
+    _dev(h, offsets, w_down, s_down, y_perm)
+    _ok("grouped_down", _lib.load().grouped_down(
+        _p(h), _p(offsets), e_count, max_rows, f, d, _p(w_down), wdt, _p(s_down), _p(y_perm),
+        _s(stream)))
+    return y_perm
+
+
 def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor,
                 out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
@@ -222,10 +262,16 @@ def tp_shard_mlp(x: torch.Tensor, w_gate_s: torch.Tensor, w_up_s: torch.Tensor,
 class MoEFFNLayer:
     """One rank's MoE FFN sub-block, FFN(RMSNorm(x)), with buffers allocated once.
 
-    ``forward`` enqueues rmsnorm -> moe_route -> moe_permute -> grouped_swiglu ->
-    moe_combine on the current stream and returns the [T, d] bf16 output (the
-    partial sum over this rank's experts [e_begin, e_begin + e_count)).
+    ``forward`` enqueues rmsnorm -> moe_route -> moe_permute -> grouped_gate_up ->
+    grouped_down (the two halves of grouped_swiglu) -> moe_combine on the
+    current stream and returns the [T, d] output (the partial sum over this
+    rank's experts [e_begin, e_begin + e_count)). ``marks``, if given, is a
+    list of 7 events recorded before each of the six stages and after the last
+    (rmsnorm's slot is recorded even when the layer has no norm).
     """
+
+    STAGES = ("rmsnorm", "moe_route", "moe_permute", "grouped_gate_up", "grouped_down",
+              "moe_combine")
 
     def __init__(self, *, T: int, d: int, f: int, w_r, bias, w_gate, w_up, w_down,
                  e_begin: int = 0, gamma=None, s_gate=None, s_up=None, s_down=None,
@@ -252,16 +298,31 @@ class MoEFFNLayer:
         self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
 
-    def forward(self, x: torch.Tensor, stream=None) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, stream=None, marks=None) -> torch.Tensor:
+        s = torch.cuda.current_stream() if stream is None else stream
+
+        def mark(i):
+            if marks is not None:
+                marks[i].record(s)
+
+        mark(0)
         v = x
         if self.gamma is not None:
-            v = rmsnorm(x, self.gamma, self.eps, out=self.v, stream=stream)
-        moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, stream=stream)
+            v = rmsnorm(x, self.gamma, self.eps, out=self.v, stream=s)
+        mark(1)
+        moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, stream=s)
+        mark(2)
         moe_permute(self.idx, self.e_begin, self.e_count, v, x_perm=self.x_perm,
                     counts=self.counts, offsets=self.offsets, src_token=self.src_token,
-                    inv_pos=self.inv_pos, workspace=self.workspace, stream=stream)
-        grouped_swiglu(self.x_perm, self.offsets, *self.w, *self.s, h_work=self.h,
-                       y_perm=self.y_perm, stream=stream)
-        return moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out, stream=stream)
+                    inv_pos=self.inv_pos, workspace=self.workspace, stream=s)
+        mark(3)
+        grouped_gate_up(self.x_perm, self.offsets, self.w[0], self.w[1], self.s[0], self.s[1],
+                        h_out=self.h, stream=s)
+        mark(4)
+        grouped_down(self.h, self.offsets, self.w[2], self.s[2], y_perm=self.y_perm, stream=s)
+        mark(5)
+        out = moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out, stream=s)
+        mark(6)
+        return out
 
     __call__ = forward

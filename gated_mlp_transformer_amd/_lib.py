@@ -29,6 +29,10 @@ _SIGNATURES = {
     "grouped_swiglu": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
                               _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_gate_up": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
+                               _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_down": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _i32,
+                            _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
                            _i32, _c_void_p]),
     "tp_shard_mlp": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
@@ -47,7 +51,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; build it with `python -m gated_mlp_transformer_amd.build` "
+            f"{LIB_PATH} is not built; build it with `python gated_mlp_transformer_amd/build.py` "
             "(hipcc, gfx950). There is no non-HIP fallback.")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():

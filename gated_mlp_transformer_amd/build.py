@@ -1,6 +1,6 @@
 """Build libmoeffn.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-    python -m gated_mlp_transformer_amd.build
+    python gated_mlp_transformer_amd/build.py
 
 Compiles every ``csrc/*.hip`` to an object under ``_build/`` and links the
 shared library next to this file. hipcc cross-compiles for gfx950, so no GPU

@@ -94,33 +94,92 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin, 
   return finish();
 }
 
+namespace {
+
+// Shared validation of the grouped GEMM calls. Returns MF_OK when the launch
+// may proceed, a status otherwise (MF_OK with *empty set for max_rows == 0).
+int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_t max_rows,
+                  int32_t d, int32_t f, int32_t w_dtype, const void* w0, const void* w1,
+                  const float* s0, const float* s1, const void* out, bool* empty) {
+  *empty = false;
+  if (!offsets || !w0 || !w1) return MF_EINVAL;
+  if (e_count < 1 || max_rows < 0 || d <= 0 || f <= 0) return MF_EINVAL;
+  if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
+  if (w_dtype == MF_FP8_E4M3 && (!s0 || !s1)) return MF_EINVAL;
+  if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 128 != 0)) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_FP8_E4M3 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
+  if (max_rows == 0) {  // zero-size buffers may be NULL
+    *empty = true;
+    return MF_OK;
+  }
+  if (!a || !out) return MF_EINVAL;
+  if (!a16(a) || !a16(w0) || !a16(w1) || !a16(out)) return MF_EUNSUPPORTED;
+  return MF_OK;
+}
+
+void enqueue_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count,
+                     int64_t max_rows, int32_t d, int32_t f, const void* w_gate, const void* w_up,
+                     int32_t w_dtype, const float* s_gate, const float* s_up, void* h,
+                     hipStream_t s) {
+  if (w_dtype == MF_BF16)
+    mf::launch_gemm_gateup_bf16(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, h,
+                                num_cus(), s);
+  else
+    mf::launch_gemm_gateup_fp8(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
+                               s_up, h, s);
+}
+
+void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t max_rows,
+                  int32_t f, int32_t d, const void* w_down, int32_t w_dtype, const float* s_down,
+                  void* y, hipStream_t s) {
+  if (w_dtype == MF_BF16)
+    mf::launch_gemm_down_bf16(h, offsets, e_count, max_rows, f, d, w_down, y, false, num_cus(),
+                              s);
+  else
+    mf::launch_gemm_down_fp8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, s);
+}
+
+}  // namespace
+
+int grouped_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count, int64_t max_rows,
+                    int32_t d, int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+                    const float* s_gate, const float* s_up, void* h_out, void* stream) {
+  bool empty;
+  const int st = check_grouped(x_perm, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up,
+                               s_gate, s_up, h_out, &empty);
+  if (st != MF_OK || empty) return st;
+  enqueue_gate_up(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, w_dtype, s_gate, s_up,
+                  h_out, S(stream));
+  return finish();
+}
+
+int grouped_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t max_rows,
+                 int32_t f, int32_t d, const void* w_down, int32_t w_dtype, const float* s_down,
+                 void* y_perm, void* stream) {
+  bool empty;
+  const int st = check_grouped(h, offsets, e_count, max_rows, d, f, w_dtype, w_down, w_down,
+                               s_down, s_down, y_perm, &empty);
+  if (st != MF_OK || empty) return st;
+  enqueue_down(h, offsets, e_count, max_rows, f, d, w_down, w_dtype, s_down, y_perm, S(stream));
+  return finish();
+}
+
 int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count, int64_t max_rows,
                    int32_t d, int32_t f, const void* w_gate, const void* w_up, const void* w_down,
                    int32_t w_dtype, const float* s_gate, const float* s_up, const float* s_down,
                    void* h_work, void* y_perm, void* stream) {
-  if (!offsets || !w_gate || !w_up || !w_down) return MF_EINVAL;
-  if (e_count < 1 || max_rows < 0 || d <= 0 || f <= 0) return MF_EINVAL;
-  if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
-  if (w_dtype == MF_FP8_E4M3 && (!s_gate || !s_up || !s_down)) return MF_EINVAL;
-  if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
-  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 128 != 0)) return MF_EUNSUPPORTED;
-  if (w_dtype == MF_FP8_E4M3 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
-  if (max_rows == 0) return MF_OK;  // zero-size buffers may be NULL
-  if (!x_perm || !h_work || !y_perm) return MF_EINVAL;
-  if (!a16(x_perm) || !a16(w_gate) || !a16(w_up) || !a16(w_down) || !a16(h_work) || !a16(y_perm))
-    return MF_EUNSUPPORTED;
+  bool empty;
+  int st = check_grouped(x_perm, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up, s_gate,
+                         s_up, h_work, &empty);
+  if (st != MF_OK || empty) return st;
+  st = check_grouped(h_work, offsets, e_count, max_rows, d, f, w_dtype, w_down, w_down, s_down,
+                     s_down, y_perm, &empty);
+  if (st != MF_OK) return st;
   const hipStream_t s = S(stream);
-  if (w_dtype == MF_BF16) {
-    const int cus = num_cus();
-    mf::launch_gemm_gateup_bf16(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, h_work,
-                                cus, s);
-    mf::launch_gemm_down_bf16(h_work, offsets, e_count, max_rows, f, d, w_down, y_perm, false,
-                              cus, s);
-  } else {
-    mf::launch_gemm_gateup_fp8(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
-                               s_up, h_work, s);
-    mf::launch_gemm_down_fp8(h_work, offsets, e_count, max_rows, f, d, w_down, s_down, y_perm, s);
-  }
+  enqueue_gate_up(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, w_dtype, s_gate, s_up,
+                  h_work, s);
+  enqueue_down(h_work, offsets, e_count, max_rows, f, d, w_down, w_dtype, s_down, y_perm, s);
   return finish();
 }
 

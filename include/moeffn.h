@@ -118,7 +118,7 @@ size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t e_count);
  * inv_pos   [T, k] i32     out: permuted row of slot (t, j), -1 if non-local
  * workspace                moe_permute_workspace_size(T, k, e_count) bytes
  * Integer results are exact and deterministic (no order-dependent atomics).
- * Requires k == 8, 1 <= e_count <= 256, e_begin >= 0, T*k < 2^31, and
+ * Requires 1 <= k <= 8, 1 <= e_count <= 256, e_begin >= 0, T*k < 2^31, and
  * (when x != NULL) d * sizeof(x_dtype) % 16 == 0.
  */
 int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
@@ -157,6 +157,27 @@ int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count,
                    const void* w_up, const void* w_down, int32_t w_dtype,
                    const float* s_gate, const float* s_up, const float* s_down,
                    void* h_work, void* y_perm, void* stream);
+
+/*
+ * grouped_gate_up - the first half of grouped_swiglu on its own:
+ *   H[o_e:o_{e+1}] = SiLU(X_perm W_gate_e) * (X_perm W_up_e)
+ * Same passages, arguments, layouts and requirements as grouped_swiglu
+ * (h_out is its h_work). The SiLU product is fused into the GEMM epilogue.
+ */
+int grouped_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count,
+                    int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
+                    const void* w_up, int32_t w_dtype, const float* s_gate,
+                    const float* s_up, void* h_out, void* stream);
+
+/*
+ * grouped_down - the second half of grouped_swiglu on its own:
+ *   Y_perm[o_e:o_{e+1}] = H[o_e:o_{e+1}] W_down_e
+ * h [max_rows, f] bf16 (grouped_gate_up's output), w_down [e_count, d, f],
+ * s_down as in grouped_swiglu, y_perm [max_rows, d] bf16. Same requirements.
+ */
+int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
+                 int64_t max_rows, int32_t f, int32_t d, const void* w_down,
+                 int32_t w_dtype, const float* s_down, void* y_perm, void* stream);
 
 /*
  * moe_combine - out[t] = sum_{j : inv_pos[t,j] >= 0} topk_w[t,j] * y_perm[inv_pos[t,j]].
