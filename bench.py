@@ -52,6 +52,9 @@ def parse():
                     help="skip the decode / dense-shard / router-only measurements")
     ap.add_argument("--only", choices=["prefill", "decode", "dense", "router"], default=None,
                     help="run one workload only (for profiling); prints its stage times")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --only: first copy a 1 GiB device buffer 3 times (a kernel of "
+                         "known traffic to scale HBM byte counters against)")
     return ap.parse_args()
 
 
@@ -288,6 +291,14 @@ def main():
     log(f"[bench] {g.version()} on {torch.cuda.get_device_name(0)}")
 
     if args.only:
+        if args.copy_calibration:
+            src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+            log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
         if args.only in ("prefill", "decode"):
             res = run_moe(PREFILL if args.only == "prefill" else DECODE, args.steps, args.warmup)
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
