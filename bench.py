@@ -205,6 +205,7 @@ def run_router(steps, warmup):
     idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
     w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
     ws = torch.empty(g.moe_permute_workspace_size(T, 8, E), dtype=torch.uint8, device="cuda")
+    rws = torch.empty(g.moe_route_workspace_size(T, d, E), dtype=torch.uint8, device="cuda")
     bufs = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
                 offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
                 src_token=torch.empty(T * 8, dtype=torch.int32, device="cuda"),
@@ -214,7 +215,7 @@ def run_router(steps, warmup):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        g.moe_route(r["x"], r["w_r"], r["bias"], 8, idx, w)
+        g.moe_route(r["x"], r["w_r"], r["bias"], 8, idx, w, rws)
         if ev:
             ev[1].record(stream)
         g.moe_permute(idx, 0, E, None, workspace=ws, **bufs)

@@ -25,7 +25,8 @@ MF_F32, MF_BF16, MF_FP8_E4M3 = 0, 1, 2
 _lib.load()  # fail loudly at import if the HIP library is missing
 
 __all__ = [
-    "MoEFFNError", "rmsnorm", "moe_route", "moe_permute_workspace_size", "moe_permute",
+    "MoEFFNError", "rmsnorm", "moe_route_workspace_size", "moe_route",
+    "moe_permute_workspace_size", "moe_permute",
     "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
     "version",
 ]
@@ -95,9 +96,13 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
     return out
 
 
+def moe_route_workspace_size(T: int, d: int, E: int) -> int:
+    return int(_lib.load().moe_route_workspace_size(T, d, E))
+
+
 def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8,
               topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
-              stream=None):
+              workspace: Optional[torch.Tensor] = None, stream=None):
     """Sigmoid-with-bias top-k router: returns (topk_idx [T,k] int32 ascending, topk_w [T,k] f32)."""
     T, d = x.shape
     E = w_r.shape[0]
@@ -105,13 +110,17 @@ def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
-    _dev(x, w_r, bias, topk_idx, topk_w)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_route_workspace_size(T, d, E)), dtype=torch.uint8,
+                                device=x.device)
+    _dev(x, w_r, bias, topk_idx, topk_w, workspace)
     if x.dtype != torch.bfloat16 or w_r.dtype != torch.bfloat16 or bias.dtype != torch.float32:
         raise ValueError("moe_route: x, w_r bf16 and bias f32")
     if w_r.shape[1] != d or bias.shape != (E,):
         raise ValueError("moe_route: w_r [E, d], bias [E]")
-    _ok("moe_route", _lib.load().moe_route(_p(x), _p(w_r), _p(bias), T, d, E, k, _p(topk_idx),
-                                           _p(topk_w), _s(stream)))
+    _ok("moe_route", _lib.load().moe_route(
+        _p(x), _p(w_r), _p(bias), T, d, E, k, _p(topk_idx), _p(topk_w), _p(workspace),
+        workspace.numel() * workspace.element_size(), _s(stream)))
     return topk_idx, topk_w
 
 
@@ -293,6 +302,8 @@ class MoEFFNLayer:
         self.inv_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.workspace = torch.empty(max(1, moe_permute_workspace_size(T, k, self.e_count)),
                                      dtype=torch.uint8, device=dev)
+        self.route_ws = torch.empty(max(1, moe_route_workspace_size(T, d, w_r.shape[0])),
+                                    dtype=torch.uint8, device=dev)
         self.x_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.h = torch.empty((rows, f), dtype=bf, device=dev)
         self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
@@ -310,7 +321,7 @@ class MoEFFNLayer:
         if self.gamma is not None:
             v = rmsnorm(x, self.gamma, self.eps, out=self.v, stream=s)
         mark(1)
-        moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, stream=s)
+        moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, self.route_ws, stream=s)
         mark(2)
         moe_permute(self.idx, self.e_begin, self.e_count, v, x_perm=self.x_perm,
                     counts=self.counts, offsets=self.offsets, src_token=self.src_token,

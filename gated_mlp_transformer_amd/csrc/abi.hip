@@ -53,16 +53,23 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d, flo
   return finish();
 }
 
+size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E) {
+  if (T < 0 || d <= 0 || d % 256 != 0 || E < 8 || E > 256 || T > kI32Max / 8) return 0;
+  return mf::route_workspace_bytes(T, d, E);
+}
+
 int moe_route(const void* x, const void* w_r, const float* bias, int64_t T, int32_t d, int32_t E,
-              int32_t k, int32_t* topk_idx, float* topk_w, void* stream) {
+              int32_t k, int32_t* topk_idx, float* topk_w, void* workspace,
+              size_t workspace_bytes, void* stream) {
   if (!w_r || !bias || T < 0 || d <= 0) return MF_EINVAL;
   if (k <= 0 || E < k) return MF_EINVAL;
-  if (k != 8 || E > 256 || d % 64 != 0) return MF_EUNSUPPORTED;
+  if (k != 8 || E > 256 || d % 256 != 0) return MF_EUNSUPPORTED;
   if (T > kI32Max / 8) return MF_EUNSUPPORTED;
   if (T == 0) return MF_OK;  // zero-size buffers may be NULL
-  if (!x || !topk_idx || !topk_w) return MF_EINVAL;
-  if (!a16(x) || !a16(w_r)) return MF_EUNSUPPORTED;
-  mf::launch_route(x, w_r, bias, T, d, E, topk_idx, topk_w, S(stream));
+  if (!x || !topk_idx || !topk_w || !workspace) return MF_EINVAL;
+  if (workspace_bytes < mf::route_workspace_bytes(T, d, E)) return MF_EINVAL;
+  if (!a16(x) || !a16(w_r) || !a16(workspace)) return MF_EUNSUPPORTED;
+  mf::launch_route(x, w_r, bias, T, d, E, topk_idx, topk_w, workspace, num_cus(), S(stream));
   return finish();
 }
 
@@ -107,7 +114,7 @@ int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_
   if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
   if (w_dtype == MF_FP8_E4M3 && (!s0 || !s1)) return MF_EINVAL;
   if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
-  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 128 != 0)) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
   if (w_dtype == MF_FP8_E4M3 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
   if (max_rows == 0) {  // zero-size buffers may be NULL
     *empty = true;
@@ -206,7 +213,7 @@ int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s, const 
   if (T > kI32Max) return MF_EUNSUPPORTED;
   if (T > 0 && (!x || !h_work || !partial)) return MF_EINVAL;  // NULL only if empty
   if (dtype == MF_BF16) {
-    if (d % 256 != 0 || f_s % 128 != 0) return MF_EUNSUPPORTED;
+    if (d % 256 != 0 || f_s % 256 != 0) return MF_EUNSUPPORTED;
     if (!a16(x) || !a16(w_gate_s) || !a16(w_up_s) || !a16(w_down_s) || !a16(h_work) ||
         !a16(partial))
       return MF_EUNSUPPORTED;

@@ -11,8 +11,11 @@ namespace mf {
 void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
                     float eps, bool bf16, hipStream_t s);
 
+int route_splits(int64_t T, int d);
+size_t route_workspace_bytes(int64_t T, int d, int E);
 void launch_route(const void* x, const void* w_r, const float* bias, int64_t T,
-                  int d, int E, int32_t* idx, float* w, hipStream_t s);
+                  int d, int E, int32_t* idx, float* w, void* workspace, int num_cus,
+                  hipStream_t s);
 
 size_t permute_workspace_bytes(int64_t T, int e_count);
 void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_count,
@@ -27,6 +30,11 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count,
                            int64_t max_rows, int K, int N, const void* w_down,
                            void* y, bool out_f32, int num_cus, hipStream_t s);
+
+// C_y = A[:, y*K/splits : (y+1)*K/splits] B[:n_valid, same]^T in fp32 for each K
+// split y (one group, bf16 operands). Requires (K / splits) % 256 == 0.
+void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b, int n_valid,
+                               int splits, float* c_partials, int num_cus, hipStream_t s);
 
 // fp8-weight (block-scaled) grouped GEMMs.
 void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count,

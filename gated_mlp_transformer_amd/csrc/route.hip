@@ -1,15 +1,17 @@
 // Sigmoid-with-bias top-8 router ("推理计算流梳理", 专家并行 / MoE Router 过程):
 //   z = x W_r^T, s = sigmoid(z), I = Top8(s + b), w_i = s_i / sum_{j in I} s_j.
 //
-// One 256-thread workgroup per 16 tokens. The logits tile [16 tokens x 256
-// experts] is computed on MFMA (bf16 operands, fp32 accumulation): wave w owns
-// experts [64w, 64w+64) as four 16x16 output tiles, so every lane keeps 16
-// logits in registers. Both operands are K-contiguous in memory (x rows and
-// W_r rows), so MFMA fragments are loaded straight from global memory, 16 bytes
-// per lane, without an LDS round trip; the A fragment (tokens) is shared by
-// all four waves through the L1. The epilogue writes s and s + b to LDS and
-// each wave selects the top 8 of four tokens by eight rounds of a wave-wide
-// arg-max on (key descending, id ascending).
+// Two kernels:
+//  1. logits: z = x W_r^T on the bf16 MFMA GEMM core (128-token tiles against
+//     all E <= 256 router rows, fp32 accumulation). The d-long contraction is
+//     split into `splits` equal ranges so that about 256 workgroups run even
+//     for a few thousand tokens; split y writes its fp32 partial logits to
+//     workspace[y][T][E]. Splitting K instead of E keeps every workgroup's
+//     W_r traffic at 1/splits of the router weight.
+//  2. select: one wavefront per token sums the partials in split order (fixed
+//     order: deterministic), applies the sigmoid and the bias, and picks the
+//     top 8 by eight rounds of a wave-wide arg-max on (key descending, id
+//     ascending); the ids are emitted ascending with w = s / sum(s).
 #include "common.h"
 #include "launch.h"
 
@@ -17,26 +19,8 @@ namespace mf {
 
 namespace {
 
-constexpr int kTok = 16;       // tokens per workgroup
-constexpr int kMaxE = 256;     // experts held by one workgroup
-constexpr int kLdsPitch = kMaxE + 4;
-
-struct Frags {
-  u32x4 a[2];
-  u32x4 b[2][4];
-};
-
-__device__ __forceinline__ void load_frags(Frags& f, const char* xrow, const char* const* wrow,
-                                           int k0, int g) {
-  // k-chunk c covers [k0 + 32c, k0 + 32c + 32); lane group g holds 8 of them.
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const size_t off = static_cast<size_t>(k0 + 32 * c + 8 * g) * 2;
-    f.a[c] = ld16(xrow + off);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[c][j] = ld16(wrow[j] + off);
-  }
-}
+constexpr int kTargetWGs = 256;   // one workgroup per CU of an MI355X
+constexpr int kTokTile = 128;     // token rows per logits tile
 
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
@@ -44,137 +28,110 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void route_kernel(const bf16_t* __restrict__ x,
-                                                    const bf16_t* __restrict__ w_r,
-                                                    const float* __restrict__ bias, int64_t T,
-                                                    int d, int E, int32_t* __restrict__ idx_out,
-                                                    float* __restrict__ w_out) {
-  __shared__ float s_lds[kTok][kLdsPitch];
-  __shared__ float k_lds[kTok][kLdsPitch];
+int route_splits(int64_t T, int d) {
+  const int64_t tiles = (T + kTokTile - 1) / kTokTile;
+  int ks = 1;  // each split's K range must stay a multiple of 256
+  while ((d / 256) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs) ks *= 2;
+  return ks;
+}
 
+size_t route_workspace_bytes(int64_t T, int d, int E) {
+  return static_cast<size_t>(route_splits(T, d)) * static_cast<size_t>(T) * E * sizeof(float);
+}
+
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ zp,
+                                                           int splits, const float* __restrict__ bias,
+                                                           int64_t T, int E,
+                                                           int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int g = lane / 16;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-
-  // A operand: token row (clamped for loads; rows >= T are never written).
-  const int64_t trow = t0 + (lane % 16) < T ? t0 + (lane % 16) : T - 1;
-  const char* xrow = reinterpret_cast<const char*>(x + trow * d);
-  // B operand: W_r rows of this wave's four 16-expert tiles (clamped).
-  const char* wrow[4];
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= T) return;
+  const int64_t split_stride = T * E;
+  float s[4], kv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = wave * 64 + j * 16 + (lane % 16);
-    wrow[j] = reinterpret_cast<const char*>(w_r + static_cast<int64_t>(e < E ? e : E - 1) * d);
-  }
-  const bool wave_active = wave * 64 < E;
-
-  f32x4 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (wave_active) {
-    Frags cur, nxt;
-    load_frags(cur, xrow, wrow, 0, g);
-    for (int k0 = 0; k0 < d; k0 += 64) {
-      if (k0 + 64 < d) load_frags(nxt, xrow, wrow, k0 + 64, g);
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(cur.a[c], cur.b[c][j], acc[j]);
-      cur = nxt;
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    float z = 0.f;
+    if (e < E) {
+      const float* p = zp + t * E + e;
+      for (int y = 0; y < splits; ++y) z += p[y * split_stride];
     }
+    s[c] = sigmoidf_(z);
+    kv[c] = e < E ? s[c] + bias[e] : -__builtin_inff();
   }
-
-  // D[token 4*(l/16)+r][expert 64w+16j+l%16]
+  int sel[8];
+  float ssel[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = wave * 64 + j * 16 + (lane % 16);
-    const float be = e < E ? bias[e] : 0.f;
+  for (int round = 0; round < 8; ++round) {
+    float bk = -__builtin_inff(), bs = 0.f;
+    int bi = 0x7fffffff;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * g + r;
-      const float s = sigmoidf_(acc[j][r]);
-      s_lds[i][e] = s;
-      k_lds[i][e] = e < E ? s + be : -__builtin_inff();
-    }
-  }
-  __syncthreads();
-
-  // Top-8 of four tokens per wave.
-  for (int ii = 0; ii < 4; ++ii) {
-    const int i = wave * 4 + ii;
-    const int64_t t = t0 + i;
-    if (t >= T) break;
-    float kv[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kv[c] = k_lds[i][lane + 64 * c];
-    int sel[8];
-#pragma unroll
-    for (int round = 0; round < 8; ++round) {
-      float bk = -__builtin_inff();
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = lane + 64 * c;
-        if (better(kv[c], e, bk, bi)) {
-          bk = kv[c];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ok = __shfl_xor(bk, m, kWave);
-        const int oi = __shfl_xor(bi, m, kWave);
-        if (better(ok, oi, bk, bi)) {
-          bk = ok;
-          bi = oi;
-        }
-      }
-      sel[round] = bi;
-      // The owner lane retires the winner.
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (lane + 64 * c == bi) kv[c] = -__builtin_inff();
-    }
-    // ids ascending (I is a set), then w = s / sum s over the set.
-#pragma unroll
-    for (int a = 1; a < 8; ++a) {
-#pragma unroll
-      for (int b = a; b > 0; --b) {
-        if (sel[b - 1] > sel[b]) {
-          const int tmp = sel[b];
-          sel[b] = sel[b - 1];
-          sel[b - 1] = tmp;
-        }
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      if (better(kv[c], e, bk, bi)) {
+        bk = kv[c];
+        bi = e;
+        bs = s[c];
       }
     }
-    float sv[8], sum = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      sv[q] = s_lds[i][clampi(sel[q], 0, kMaxE - 1)];
-      sum += sv[q];
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ok = __shfl_xor(bk, m, kWave);
+      const int oi = __shfl_xor(bi, m, kWave);
+      const float os = __shfl_xor(bs, m, kWave);
+      if (better(ok, oi, bk, bi)) {
+        bk = ok;
+        bi = oi;
+        bs = os;
+      }
     }
-    if (lane < 8) {
-      int mine = sel[0];
-      float ms = sv[0];
+    sel[round] = bi;
+    ssel[round] = bs;
 #pragma unroll
-      for (int q = 1; q < 8; ++q)
-        if (lane == q) {
-          mine = sel[q];
-          ms = sv[q];
-        }
-      idx_out[t * 8 + lane] = mine;
-      w_out[t * 8 + lane] = ms / sum;
+    for (int c = 0; c < 4; ++c)
+      if (lane + 64 * c == bi) kv[c] = -__builtin_inff();  // the owner lane retires the winner
+  }
+  // ids ascending (I is a set), scores carried along
+#pragma unroll
+  for (int a = 1; a < 8; ++a) {
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      if (sel[b - 1] > sel[b]) {
+        const int ti = sel[b];
+        sel[b] = sel[b - 1];
+        sel[b - 1] = ti;
+        const float ts = ssel[b];
+        ssel[b] = ssel[b - 1];
+        ssel[b - 1] = ts;
+      }
     }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) sum += ssel[q];
+  if (lane < 8) {
+    int mine = sel[0];
+    float ms = ssel[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q)
+      if (lane == q) {
+        mine = sel[q];
+        ms = ssel[q];
+      }
+    idx_out[t * 8 + lane] = mine;
+    w_out[t * 8 + lane] = ms / sum;
   }
 }
 
 void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, int d, int E,
-                  int32_t* idx, float* w, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
-  route_kernel<<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x),
-                                    static_cast<const bf16_t*>(w_r), bias, T, d, E, idx, w);
+                  int32_t* idx, float* w, void* workspace, int num_cus, hipStream_t s) {
+  const int splits = route_splits(T, d);
+  float* zp = static_cast<float*>(workspace);
+  launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
+  route_select_kernel<<<dim3(static_cast<unsigned>((T + 3) / 4)), 256, 0, s>>>(zp, splits, bias,
+                                                                               T, E, idx, w);
 }
 
 }  // namespace mf

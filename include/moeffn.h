@@ -69,6 +69,13 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
             float eps, int32_t dtype, void* stream);
 
 /*
+ * moe_route_workspace_size - bytes of device workspace moe_route needs for
+ * T tokens, hidden size d and E experts (fp32 partial logits). Depends on
+ * (T, d, E) only. Returns 0 for arguments moe_route would reject.
+ */
+size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E);
+
+/*
  * moe_route - sigmoid-with-bias top-k expert router.
  *
  * "推理计算流梳理", 专家并行 / MoE Router 过程, router equation:
@@ -81,13 +88,16 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
  * topk_idx [T, k] int32     out: the k selected expert ids of each token, in
  *                           ascending order (I is a set)
  * topk_w   [T, k] f32       out: w_i aligned with topk_idx; each row sums to 1
- * Logits are bf16 x bf16 products accumulated in fp32 (MFMA); s, s + b and
- * w are fp32. Ties in s + b go to the lower expert id.
- * Requires k == 8, 8 <= E <= 256, d % 64 == 0.
+ * workspace                 moe_route_workspace_size(T, d, E) bytes; its
+ *                           content on entry does not matter
+ * Logits are bf16 x bf16 products accumulated in fp32 on MFMA (the d-long
+ * contraction may be split into ranges whose fp32 partial sums are added in a
+ * fixed order); s, s + b and w are fp32. Ties in s + b go to the lower id.
+ * Requires k == 8, 8 <= E <= 256, d % 256 == 0.
  */
 int moe_route(const void* x, const void* w_r, const float* bias, int64_t T,
               int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
-              void* stream);
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_permute_workspace_size - bytes of device workspace moe_permute needs.
@@ -149,7 +159,7 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
  * GEMMs run on MFMA with bf16 operands and fp32 accumulation; SiLU(g)*u is
  * fused into the gate/up epilogue in fp32. fp8 codes are converted to bf16
  * exactly and each 128-deep partial sum is scaled in fp32.
- * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 128 == 0;
+ * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 256 == 0;
  * fp8: d % 256 == 0 and f % 256 == 0.
  */
 int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count,
@@ -211,7 +221,7 @@ int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
  * h_work   [T, f_s]  dtype, out: H_i
  * partial  [T, d]    f32, out: P_i, the full-shape partial sum
  * dtype MF_BF16 (MFMA, fp32 accumulation; H_i rounded to bf16; requires
- * d % 256 == 0, f_s % 128 == 0) or MF_F32 (fp32 FMA throughout; any sizes).
+ * d % 256 == 0, f_s % 256 == 0) or MF_F32 (fp32 FMA throughout; any sizes).
  */
 int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s,
                  const void* w_down_s, int64_t T, int32_t d, int32_t f_s,

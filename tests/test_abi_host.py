@@ -70,13 +70,19 @@ def test_rmsnorm_validation(lib):
 
 
 def test_route_validation(lib):
-    assert lib.moe_route(P, P, N, 4, 64, 256, 8, P, P, N) == MF_EINVAL
-    assert lib.moe_route(P, P, P, 4, 64, 7, 8, P, P, N) == MF_EINVAL      # E < k
-    assert lib.moe_route(P, P, P, 4, 64, 256, 0, P, P, N) == MF_EINVAL
-    assert lib.moe_route(P, P, P, 4, 64, 256, 6, P, P, N) == MF_EUNSUPPORTED  # k != 8
-    assert lib.moe_route(P, P, P, 4, 64, 257, 8, P, P, N) == MF_EUNSUPPORTED
-    assert lib.moe_route(P, P, P, 4, 96, 256, 8, P, P, N) == MF_EUNSUPPORTED
-    assert lib.moe_route(P, P, P, 0, 64, 256, 8, P, P, N) == MF_OK
+    ws = lib.moe_route_workspace_size(4, 256, 256)
+    assert ws > 0 and lib.moe_route_workspace_size(4, 64, 256) == 0
+    call = lambda x=P, b=P, T=4, d=256, E=256, k=8, wsp=P, wsb=ws: lib.moe_route(  # noqa: E731
+        x, P, b, T, d, E, k, P, P, wsp, wsb, N)
+    assert call(b=N) == MF_EINVAL
+    assert call(E=7) == MF_EINVAL                 # E < k
+    assert call(k=0) == MF_EINVAL
+    assert call(wsp=N) == MF_EINVAL
+    assert call(wsb=ws - 4) == MF_EINVAL
+    assert call(k=6) == MF_EUNSUPPORTED           # k != 8
+    assert call(E=257) == MF_EUNSUPPORTED
+    assert call(d=64) == MF_EUNSUPPORTED          # d % 256
+    assert call(T=0, x=N, wsp=N, wsb=0) == MF_OK
 
 
 def test_permute_validation(lib):
@@ -101,15 +107,16 @@ def test_permute_validation(lib):
 
 
 def test_grouped_swiglu_validation(lib):
-    def call(ec=4, rows=64, d=256, f=128, wdt=BF16, s=(N, N, N), x=P):
+    def call(ec=4, rows=64, d=256, f=256, wdt=BF16, s=(N, N, N), x=P):
         return lib.grouped_swiglu(x, P, ec, rows, d, f, P, P, P, wdt, *s, P, P, N)
     assert call(x=N) == MF_EINVAL
     assert call(ec=0) == MF_EINVAL
     assert call(wdt=F32) == MF_EINVAL
     assert call(wdt=FP8) == MF_EINVAL                      # fp8 needs scales
     assert call(d=128) == MF_EUNSUPPORTED                  # bf16 needs d % 256
-    assert call(f=64) == MF_EUNSUPPORTED                   # bf16 needs f % 128
-    assert call(wdt=FP8, s=(P, P, P)) == MF_EUNSUPPORTED   # fp8 needs f % 256
+    assert call(f=64) == MF_EUNSUPPORTED                   # bf16 needs f % 256
+    assert call(f=384) == MF_EUNSUPPORTED
+    assert call(wdt=FP8, s=(P, P, P), f=384) == MF_EUNSUPPORTED   # fp8 needs f % 256
     assert call(ec=300) == MF_EUNSUPPORTED
     assert call(rows=0) == MF_OK
 
@@ -120,7 +127,8 @@ def test_combine_and_shard_validation(lib):
     assert lib.moe_combine(P, P, P, 4, 8, 72, 32, P, BF16, N) == MF_EUNSUPPORTED
     assert lib.moe_combine(P, P, P, 4, 8, 64, 32, P, FP8, N) == MF_EINVAL
     assert lib.moe_combine(P, P, P, 0, 8, 64, 32, P, BF16, N) == MF_OK
-    assert lib.tp_shard_mlp(P, P, P, N, 4, 256, 128, BF16, P, P, N) == MF_EINVAL
-    assert lib.tp_shard_mlp(P, P, P, P, 4, 192, 128, BF16, P, P, N) == MF_EUNSUPPORTED
-    assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 128, FP8, P, P, N) == MF_EINVAL
+    assert lib.tp_shard_mlp(P, P, P, N, 4, 256, 256, BF16, P, P, N) == MF_EINVAL
+    assert lib.tp_shard_mlp(P, P, P, P, 4, 192, 256, BF16, P, P, N) == MF_EUNSUPPORTED
+    assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 128, BF16, P, P, N) == MF_EUNSUPPORTED
+    assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 256, FP8, P, P, N) == MF_EINVAL
     assert lib.tp_shard_mlp(P, P, P, P, 0, 64, 64, F32, P, P, N) == MF_OK

@@ -63,8 +63,9 @@ def test_rmsnorm_in_place(g):
 
 # -------------------------------------------------------------------- route --
 
-@pytest.mark.parametrize("T,d,E", [(1, 64, 8), (37, 256, 12), (300, 256, 64), (257, 512, 256),
-                                   (64, 4096, 256), (1000, 1024, 200)])
+@pytest.mark.parametrize("T,d,E", [(1, 256, 8), (37, 256, 12), (300, 256, 64), (257, 512, 256),
+                                   (64, 4096, 256), (1000, 1024, 200), (4096, 768, 9),
+                                   (129, 2048, 100)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
     idx, w = g.moe_route(r["x"], r["w_r"], r["bias"])
@@ -161,10 +162,12 @@ def _oracle_weights(W, e, wdtype):
 
 
 @pytest.mark.parametrize("wdtype,counts,d,f", [
-    ("bf16", [0, 1, 130, 257, 3], 256, 384),
+    ("bf16", [0, 1, 130, 257, 3], 256, 768),
     ("bf16", [200, 0, 0, 7], 512, 256),
-    ("bf16", [1000], 256, 128),
-    ("bf16", [0, 0, 0], 256, 128),
+    ("bf16", [1000], 256, 256),
+    ("bf16", [0, 0, 0], 256, 256),
+    ("bf16", [1, 33, 65, 97, 128, 129, 31, 32], 256, 256),   # every tail sub-tile count
+    ("bf16", [300] * 5 + [0, 77, 513] + [300] * 8, 1024, 1024),  # > 256 tiles: several rounds
     ("fp8", [1, 3, 0, 17, 2, 16], 256, 512),
     ("fp8", [40], 512, 256),
 ])
@@ -250,7 +253,7 @@ def test_tp_shard_f32_dense_config(g):
               rel=1e-5, max_abs=1e-6)
 
 
-@pytest.mark.parametrize("T,d,f,p", [(300, 256, 512, 2), (129, 512, 256, 1), (1, 256, 128, 1)])
+@pytest.mark.parametrize("T,d,f,p", [(300, 256, 512, 2), (129, 512, 256, 1), (1, 256, 256, 1)])
 def test_tp_shard_bf16(g, T, d, f, p):
     D = make_dense(T, d, f, dtype=torch.bfloat16, device=DEV, w_std=0.05)
     xf = to_f64(D["x"])
