@@ -161,6 +161,7 @@ def run_dense(steps, warmup):
     spec = synth.WORKLOADS[DENSE]
     T, d, f = spec["T"], spec["d"], spec["f"]
     D = make_dense(T, d, f, dtype=torch.bfloat16, norm=True, device="cuda")
+    packed = [g.pack_weights(D[k]) for k in ("w_gate", "w_up", "w_down")]
     v = torch.empty_like(D["x"])
     h = torch.empty((T, f), dtype=torch.bfloat16, device="cuda")
     part = torch.empty((T, d), dtype=torch.float32, device="cuda")
@@ -172,7 +173,7 @@ def run_dense(steps, warmup):
         g.rmsnorm(D["x"], D["gamma"], 1e-5, out=v)
         if ev:
             ev[1].record(stream)
-        g.tp_shard_mlp(v, D["w_gate"], D["w_up"], D["w_down"], h_work=h, partial=part)
+        g.tp_shard_mlp(v, *packed, h_work=h, partial=part)
         if ev:
             ev[2].record(stream)
 
@@ -202,6 +203,7 @@ def run_router(steps, warmup):
     spec = synth.WORKLOADS[ROUTER]
     T, d, E = spec["T"], spec["d"], spec["E"]
     r = make_router(T, d, E, device="cuda")
+    w_r = g.pack_weights(r["w_r"])
     idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
     w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
     ws = torch.empty(g.moe_permute_workspace_size(T, 8, E), dtype=torch.uint8, device="cuda")
@@ -215,7 +217,7 @@ def run_router(steps, warmup):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        g.moe_route(r["x"], r["w_r"], r["bias"], 8, idx, w, rws)
+        g.moe_route(r["x"], w_r, r["bias"], 8, idx, w, rws)
         if ev:
             ev[1].record(stream)
         g.moe_permute(idx, 0, E, None, workspace=ws, **bufs)

@@ -7,8 +7,10 @@ passed in (torch supplies device memory), and passes raw pointers and the
 current HIP stream to the library. Every step of the computation runs in the
 library's HIP kernels; nothing here computes, and there is no fallback.
 
-Weights are stored [out_features, in_features]: w_gate / w_up are
-[E, f, d] and w_down is [E, d, f] (the transpose of the pages' W in Y = X W).
+Weights are given [out_features, in_features]: w_gate / w_up are
+[E, f, d] and w_down is [E, d, f] (the transpose of the pages' W in Y = X W),
+and are packed once with ``pack_weights`` into the MFMA fragment order the
+GEMMs read; the GEMM calls take the ``PackedWeights`` it returns.
 """
 
 from __future__ import annotations
@@ -25,7 +27,8 @@ MF_F32, MF_BF16, MF_FP8_E4M3 = 0, 1, 2
 _lib.load()  # fail loudly at import if the HIP library is missing
 
 __all__ = [
-    "MoEFFNError", "rmsnorm", "moe_route_workspace_size", "moe_route",
+    "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "moe_route_workspace_size",
+    "moe_route",
     "moe_permute_workspace_size", "moe_permute",
     "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
     "version",
@@ -96,6 +99,36 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
     return out
 
 
+class PackedWeights(NamedTuple):
+    """Weights [groups, N, K] rearranged by pack_weights (flat bytes on the device)."""
+    data: torch.Tensor   # uint8, packed_weights_bytes(groups, N, K, dtype) bytes
+    dtype: torch.dtype   # torch.bfloat16 or torch.float8_e4m3fn
+    groups: int
+    N: int
+    K: int
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> PackedWeights:
+    """Pack w ([groups, N, K] or [N, K], bf16 or float8_e4m3fn) for the GEMM calls."""
+    w3 = w.unsqueeze(0) if w.dim() == 2 else w
+    G, N, K = w3.shape
+    code = _dtype_code(w3.dtype)
+    nbytes = int(_lib.load().packed_weights_bytes(G, N, K, code))
+    if nbytes == 0:
+        raise ValueError(f"pack_weights: unsupported shape/dtype {tuple(w3.shape)} {w3.dtype}")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w3.device)
+    _dev(w3, out)
+    _ok("pack_weights", _lib.load().pack_weights(_p(w3), _p(out), G, N, K, code, _s(stream)))
+    return PackedWeights(out, w3.dtype, G, N, K)
+
+
+def _pw(w, name: str) -> PackedWeights:
+    if not isinstance(w, PackedWeights):
+        raise TypeError(f"{name}: pass weights packed by pack_weights()")
+    _dev(w.data)
+    return w
+
+
 def moe_route_workspace_size(T: int, d: int, E: int) -> int:
     return int(_lib.load().moe_route_workspace_size(T, d, E))
 
@@ -105,7 +138,8 @@ def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8
               workspace: Optional[torch.Tensor] = None, stream=None):
     """Sigmoid-with-bias top-k router: returns (topk_idx [T,k] int32 ascending, topk_w [T,k] f32)."""
     T, d = x.shape
-    E = w_r.shape[0]
+    w_r = _pw(w_r, "moe_route")
+    E = w_r.N
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
@@ -113,13 +147,13 @@ def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8
     if workspace is None:
         workspace = torch.empty(max(1, moe_route_workspace_size(T, d, E)), dtype=torch.uint8,
                                 device=x.device)
-    _dev(x, w_r, bias, topk_idx, topk_w, workspace)
+    _dev(x, bias, topk_idx, topk_w, workspace)
     if x.dtype != torch.bfloat16 or w_r.dtype != torch.bfloat16 or bias.dtype != torch.float32:
         raise ValueError("moe_route: x, w_r bf16 and bias f32")
-    if w_r.shape[1] != d or bias.shape != (E,):
+    if w_r.groups != 1 or w_r.K != d or tuple(bias.shape) != (E,):
         raise ValueError("moe_route: w_r [E, d], bias [E]")
     _ok("moe_route", _lib.load().moe_route(
-        _p(x), _p(w_r), _p(bias), T, d, E, k, _p(topk_idx), _p(topk_w), _p(workspace),
+        _p(x), _p(w_r.data), _p(bias), T, d, E, k, _p(topk_idx), _p(topk_w), _p(workspace),
         workspace.numel() * workspace.element_size(), _s(stream)))
     return topk_idx, topk_w
 
@@ -172,26 +206,27 @@ def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Te
                    s_down=None, *, h_work=None, y_perm=None, stream=None):
     """Grouped expert gated MLPs over expert-contiguous rows. Returns (y_perm, h_work)."""
     max_rows, d = x_perm.shape
-    e_count, f, d2 = w_gate.shape
-    if d2 != d or w_up.shape != w_gate.shape or tuple(w_down.shape) != (e_count, d, f):
+    w_gate, w_up, w_down = (_pw(w, "grouped_swiglu") for w in (w_gate, w_up, w_down))
+    e_count, f, d2 = w_gate.groups, w_gate.N, w_gate.K
+    if (d2 != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d)
+            or (w_down.groups, w_down.N, w_down.K) != (e_count, d, f)):
         raise ValueError("grouped_swiglu: w_gate/w_up [E, f, d], w_down [E, d, f]")
     if offsets.numel() != e_count + 1 or offsets.dtype != torch.int32:
         raise ValueError("grouped_swiglu: offsets [E+1] int32")
-    wdt = _dtype_code(w_gate.dtype)
-    if w_up.dtype != w_gate.dtype or w_down.dtype != w_gate.dtype:
-        raise ValueError("grouped_swiglu: one weight dtype")
+    wdt = _grouped_dtype(w_gate, w_up, w_down)
     if h_work is None:
         h_work = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=x_perm.device)
-    _dev(x_perm, offsets, w_gate, w_up, w_down, s_gate, s_up, s_down, h_work, y_perm)
+    _dev(x_perm, offsets, s_gate, s_up, s_down, h_work, y_perm)
     _ok("grouped_swiglu", _lib.load().grouped_swiglu(
-        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate), _p(w_up), _p(w_down), wdt,
+        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate.data), _p(w_up.data),
+        _p(w_down.data), wdt,
         _p(s_gate), _p(s_up), _p(s_down), _p(h_work), _p(y_perm), _s(stream)))
     return y_perm, h_work
 
 
-def _grouped_dtype(w_gate, *rest):
+def _grouped_dtype(w_gate: PackedWeights, *rest: PackedWeights) -> int:
     wdt = _dtype_code(w_gate.dtype)
     if any(w.dtype != w_gate.dtype for w in rest):
         raise ValueError("grouped GEMM: one weight dtype")
@@ -205,13 +240,16 @@ def grouped_gate_up(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.T
                     stream=None) -> torch.Tensor:
     """H = SiLU(X_perm W_gate_e) * (X_perm W_up_e) per expert segment. Returns h_out."""
     max_rows, d = x_perm.shape
-    e_count, f, _ = w_gate.shape
+    w_gate, w_up = _pw(w_gate, "grouped_gate_up"), _pw(w_up, "grouped_gate_up")
+    e_count, f = w_gate.groups, w_gate.N
+    if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
+        raise ValueError("grouped_gate_up: w_gate/w_up [E, f, d]")
     wdt = _grouped_dtype(w_gate, w_up)
     if h_out is None:
         h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
-    _dev(x_perm, offsets, w_gate, w_up, s_gate, s_up, h_out)
+    _dev(x_perm, offsets, s_gate, s_up, h_out)
     _ok("grouped_gate_up", _lib.load().grouped_gate_up(
-        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate), _p(w_up), wdt,
+        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate.data), _p(w_up.data), wdt,
         _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
     return h_out
 
@@ -220,13 +258,16 @@ def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s
                  y_perm=None, stream=None) -> torch.Tensor:
     """Y_perm = H W_down_e per expert segment. Returns y_perm."""
     max_rows, f = h.shape
-    e_count, d, _ = w_down.shape
+    w_down = _pw(w_down, "grouped_down")
+    e_count, d = w_down.groups, w_down.N
+    if w_down.K != f:
+        raise ValueError("grouped_down: w_down [E, d, f]")
     wdt = _grouped_dtype(w_down)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=h.device)
-    _dev(h, offsets, w_down, s_down, y_perm)
+    _dev(h, offsets, s_down, y_perm)
     _ok("grouped_down", _lib.load().grouped_down(
-        _p(h), _p(offsets), e_count, max_rows, f, d, _p(w_down), wdt, _p(s_down), _p(y_perm),
+        _p(h), _p(offsets), e_count, max_rows, f, d, _p(w_down.data), wdt, _p(s_down), _p(y_perm),
         _s(stream)))
     return y_perm
 
@@ -250,17 +291,26 @@ def tp_shard_mlp(x: torch.Tensor, w_gate_s: torch.Tensor, w_up_s: torch.Tensor,
                  w_down_s: torch.Tensor, *, h_work=None, partial=None, stream=None):
     """One TP shard of the dense gated MLP. Returns (partial f32 [T,d], h_work [T,f_s])."""
     T, d = x.shape
-    fs = w_gate_s.shape[0]
-    if (tuple(w_gate_s.shape) != (fs, d) or tuple(w_up_s.shape) != (fs, d)
-            or tuple(w_down_s.shape) != (d, fs)):
-        raise ValueError("tp_shard_mlp: w_gate_s/w_up_s [f_s, d], w_down_s [d, f_s]")
+    if x.dtype == torch.bfloat16:
+        w_gate_s, w_up_s, w_down_s = (_pw(w, "tp_shard_mlp") for w in (w_gate_s, w_up_s, w_down_s))
+        fs = w_gate_s.N
+        shapes = [(w.groups, w.N, w.K) for w in (w_gate_s, w_up_s, w_down_s)]
+        if shapes != [(1, fs, d), (1, fs, d), (1, d, fs)]:
+            raise ValueError("tp_shard_mlp: w_gate_s/w_up_s [f_s, d], w_down_s [d, f_s]")
+        ptrs = [w.data for w in (w_gate_s, w_up_s, w_down_s)]
+    else:
+        fs = w_gate_s.shape[0]
+        if (tuple(w_gate_s.shape) != (fs, d) or tuple(w_up_s.shape) != (fs, d)
+                or tuple(w_down_s.shape) != (d, fs)):
+            raise ValueError("tp_shard_mlp: w_gate_s/w_up_s [f_s, d], w_down_s [d, f_s]")
+        ptrs = [w_gate_s, w_up_s, w_down_s]
     if h_work is None:
         h_work = torch.empty((T, fs), dtype=x.dtype, device=x.device)
     if partial is None:
         partial = torch.empty((T, d), dtype=torch.float32, device=x.device)
-    _dev(x, w_gate_s, w_up_s, w_down_s, h_work, partial)
+    _dev(x, *ptrs, h_work, partial)
     _ok("tp_shard_mlp", _lib.load().tp_shard_mlp(
-        _p(x), _p(w_gate_s), _p(w_up_s), _p(w_down_s), T, d, fs, _dtype_code(x.dtype),
+        _p(x), _p(ptrs[0]), _p(ptrs[1]), _p(ptrs[2]), T, d, fs, _dtype_code(x.dtype),
         _p(h_work), _p(partial), _s(stream)))
     return partial, h_work
 
@@ -285,11 +335,14 @@ class MoEFFNLayer:
     def __init__(self, *, T: int, d: int, f: int, w_r, bias, w_gate, w_up, w_down,
                  e_begin: int = 0, gamma=None, s_gate=None, s_up=None, s_down=None,
                  k: int = 8, eps: float = 1e-5, out_dtype=torch.bfloat16):
+        """Weights are given [out, in] (w_r [E, d], w_gate/w_up [E_loc, f, d],
+        w_down [E_loc, d, f]) and packed here, once."""
         dev = w_r.device
         self.T, self.d, self.f, self.k, self.eps = T, d, f, k, eps
         self.e_begin, self.e_count = e_begin, w_gate.shape[0]
-        self.gamma, self.w_r, self.bias = gamma, w_r, bias
-        self.w = (w_gate, w_up, w_down)
+        self.gamma, self.bias = gamma, bias
+        self.w_r = pack_weights(w_r)
+        self.w = tuple(pack_weights(w) for w in (w_gate, w_up, w_down))
         self.s = (s_gate, s_up, s_down)
         bf = torch.bfloat16
         rows = T * k
@@ -302,7 +355,7 @@ class MoEFFNLayer:
         self.inv_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.workspace = torch.empty(max(1, moe_permute_workspace_size(T, k, self.e_count)),
                                      dtype=torch.uint8, device=dev)
-        self.route_ws = torch.empty(max(1, moe_route_workspace_size(T, d, w_r.shape[0])),
+        self.route_ws = torch.empty(max(1, moe_route_workspace_size(T, d, self.w_r.N)),
                                     dtype=torch.uint8, device=dev)
         self.x_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.h = torch.empty((rows, f), dtype=bf, device=dev)

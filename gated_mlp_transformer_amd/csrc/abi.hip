@@ -53,6 +53,26 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d, flo
   return finish();
 }
 
+size_t packed_weights_bytes(int64_t groups, int32_t N, int32_t K, int32_t dtype) {
+  if (groups < 0 || N <= 0 || K <= 0) return 0;
+  if (dtype == MF_BF16 && K % 16 == 0) return mf::packed_bytes(groups, N, K, false);
+  if (dtype == MF_FP8_E4M3 && K % 128 == 0) return mf::packed_bytes(groups, N, K, true);
+  return 0;
+}
+
+int pack_weights(const void* src, void* dst, int64_t groups, int32_t N, int32_t K, int32_t dtype,
+                 void* stream) {
+  if (groups < 0 || N <= 0 || K <= 0) return MF_EINVAL;
+  if (dtype != MF_BF16 && dtype != MF_FP8_E4M3) return MF_EINVAL;
+  if ((dtype == MF_BF16 && K % 16 != 0) || (dtype == MF_FP8_E4M3 && K % 128 != 0))
+    return MF_EUNSUPPORTED;
+  if (groups == 0) return MF_OK;
+  if (!src || !dst) return MF_EINVAL;
+  if (!a16(src) || !a16(dst)) return MF_EUNSUPPORTED;
+  mf::launch_pack(src, dst, groups, N, K, dtype == MF_FP8_E4M3, S(stream));
+  return finish();
+}
+
 size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E) {
   if (T < 0 || d <= 0 || d % 256 != 0 || E < 8 || E > 256 || T > kI32Max / 8) return 0;
   return mf::route_workspace_bytes(T, d, E);

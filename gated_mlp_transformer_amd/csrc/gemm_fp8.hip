@@ -11,12 +11,13 @@
 // columns), each wave 64 columns as four 16-row weight sub-tiles (eight for
 // gate + up). The weight sub-tile is the MFMA's first operand; the expert's
 // rows (up to 16 per pass, zero-padded) are the second. Every lane loads 32
-// contiguous weight bytes of a 128-deep slab per sub-tile, so a row's 128-byte
-// slab is read by one pair of 16-byte loads across the four lane groups; the
-// contraction index is permuted identically on both operands (lane group g,
-// MFMA c, element v <-> k = 32g + 8c + v), which leaves the dot products
-// unchanged. Codes are converted to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8
-// with a unit scale), each slab is accumulated on MFMA in fp32 from zero, and
+// weight bytes of a 128-deep slab per sub-tile (row l%16, bytes 32(l/16) +
+// 0..31), from weights packed so that each of its two 16-byte loads is one
+// contiguous 1 KB across the wave; the contraction index is permuted
+// identically on both operands (lane group g, MFMA c, element v <-> k =
+// 32g + 8c + v), which leaves the dot products unchanged. Codes are converted
+// to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with a unit scale), each slab is
+// accumulated on MFMA in fp32 from zero, and
 // the slab sum is scaled by its block's fp32 scale into the running fp32 sum.
 // The next slab's loads are issued before the current slab is consumed.
 // Experts with more than 16 rows are processed 16 rows at a time (the weights
@@ -33,8 +34,8 @@ constexpr int SLAB = 128; // K depth per scale block
 
 struct Fp8Params {
   const char* a;           // [max_rows, K] bf16
-  const uint8_t* b0;       // [groups, N, K] fp8 (gate, or down)
-  const uint8_t* b1;       // [groups, N, K] fp8 (up; gated only)
+  const uint8_t* b0;       // packed fp8 weights (gate, or down), see pack.hip
+  const uint8_t* b1;       // packed fp8 weights (up; gated only)
   const float* s0;         // [groups, N/128, K/128]
   const float* s1;
   char* c;                 // [max_rows, N] bf16
@@ -69,12 +70,17 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
   const int kslabs = p.K / SLAB;
   const int64_t K = p.K;
 
+  // Packed fp8 weights: 16-row x 128-column blocks of 2 KB, [half][lane][16 B];
+  // lane l's two 16-byte loads of a block are row l%16, bytes 32(l/16) + 0..31
+  // of the block's 128-byte slab, each load one contiguous 1 KB across lanes.
+  const int kblocks = p.K / SLAB;
   const uint8_t* wp[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
     const uint8_t* base = (GATED && q >= 4) ? p.b1 : p.b0;
-    const int n = n0w + 16 * (q & 3) + lr;
-    wp[q] = base + (static_cast<int64_t>(e) * p.N + n) * K + 32 * lg;
+    const int nb = (n0w >> 4) + (q & 3);
+    wp[q] = base + ((static_cast<int64_t>(e) * (p.N / 16) + nb) * kblocks) * 2048 +
+            lane * 16;
   }
   const int64_t sbase = (static_cast<int64_t>(e) * (p.N / SLAB) + n0w / SLAB) * kslabs;
   const float* sp0 = p.s0 + sbase;
@@ -92,10 +98,11 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
     SlabRegs<R> cur, nxt;
     auto load = [&](SlabRegs<R>& s, int kb) {
       const int64_t kofs = static_cast<int64_t>(kb) * SLAB;
+      const int64_t bofs = static_cast<int64_t>(kb) * 2048;
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        s.b[q][0] = ld16(wp[q] + kofs);
-        s.b[q][1] = ld16(wp[q] + kofs + 16);
+        s.b[q][0] = ld16(wp[q] + bofs);
+        s.b[q][1] = ld16(wp[q] + bofs + 1024);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c)

@@ -23,7 +23,13 @@ void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_cou
                     int32_t* offsets, int32_t* src_token, int32_t* inv_pos,
                     void* workspace, hipStream_t s);
 
-// bf16 MFMA grouped GEMMs. offsets == nullptr means one group of max_rows rows.
+// Weight packing into MFMA fragment order (pack.hip).
+size_t packed_bytes(int64_t groups, int N, int K, bool fp8);
+void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8,
+                 hipStream_t s);
+
+// bf16 MFMA grouped GEMMs on packed weights. offsets == nullptr means one group
+// of max_rows rows.
 void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
                              int64_t max_rows, int K, int N, const void* w_gate,
                              const void* w_up, void* h, int num_cus, hipStream_t s);

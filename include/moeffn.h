@@ -18,9 +18,13 @@
  *    the null stream). They never synchronise the host, never allocate device
  *    memory and keep no mutable global state, so they are re-entrant. Calls
  *    that share an output or workspace buffer must be ordered by the caller.
- *  - Linear-layer weights are stored [out_features, in_features] (each output
- *    feature's weights contiguous), i.e. the transpose of the pages' W in
- *    Y = X W. The router weight W_r is [E, d], as in the pages' z = x W_r^T.
+ *  - Linear-layer weights are given as [out_features, in_features] (each
+ *    output feature's weights contiguous), i.e. the transpose of the pages' W
+ *    in Y = X W; the router weight W_r is [E, d], as in the pages' z = x W_r^T.
+ *    Every weight argument of the GEMM calls (W_r, the experts' W_gate, W_up,
+ *    W_down and the TP shards) is passed PACKED by pack_weights, once, ahead
+ *    of use: a layout in which each MFMA weight fragment is one contiguous
+ *    1 KB block (see pack_weights).
  *  - Return value: MF_OK (0), MF_EINVAL (-1: null pointer, bad size or value),
  *    MF_EUNSUPPORTED (-2: valid but outside what the kernels implement, such
  *    as a dtype combination, an alignment or a dimension that is not a
@@ -69,6 +73,30 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
             float eps, int32_t dtype, void* stream);
 
 /*
+ * packed_weights_bytes - bytes of pack_weights' output for `groups` weight
+ * matrices of N rows and K columns (dtype MF_BF16 or MF_FP8_E4M3). Returns 0
+ * for arguments pack_weights would reject.
+ */
+size_t packed_weights_bytes(int64_t groups, int32_t N, int32_t K, int32_t dtype);
+
+/*
+ * pack_weights - rearranges src [groups, N, K] (row-major, [out, in]) into the
+ * order the GEMM calls consume, dst (packed_weights_bytes bytes). A pure
+ * permutation plus zero padding of the last row block; the values are
+ * unchanged. Weights are packed once, when they are loaded, not per call.
+ *
+ *   MF_BF16: 32-row x 16-column fragments of 1 KB, row block major:
+ *     dst[g][nb][kb][l][v] = W[g][32 nb + l % 32][16 kb + 8 (l / 32) + v]
+ *     (l = 0..63, v = 0..7; rows >= N read as 0). Requires K % 16 == 0.
+ *   MF_FP8_E4M3 (codes; block scales are not packed): 16-row x 128-column
+ *     blocks of 2 KB, each two 1 KB halves:
+ *     dst[g][nb][kb][h][l][b] = W[g][16 nb + l % 16][128 kb + 32 (l / 16) + 16 h + b]
+ *     (h = 0..1, l = 0..63, b = 0..15; rows >= N read as 0). Requires K % 128 == 0.
+ */
+int pack_weights(const void* src, void* dst, int64_t groups, int32_t N, int32_t K,
+                 int32_t dtype, void* stream);
+
+/*
  * moe_route_workspace_size - bytes of device workspace moe_route needs for
  * T tokens, hidden size d and E experts (fp32 partial logits). Depends on
  * (T, d, E) only. Returns 0 for arguments moe_route would reject.
@@ -83,7 +111,7 @@ size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E);
  * The bias only selects experts; the weights use the unbiased scores.
  *
  * x        [T, d] bf16      router input (RMSNorm output inside the FFN block)
- * w_r      [E, d] bf16      router weight
+ * w_r      [E, d] bf16      router weight, packed (pack_weights, MF_BF16)
  * bias     [E]    f32
  * topk_idx [T, k] int32     out: the k selected expert ids of each token, in
  *                           ascending order (I is a set)
@@ -148,8 +176,8 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
  *
  * x_perm   [max_rows, d] bf16    rows grouped by expert (moe_permute output)
  * offsets  [e_count+1] int32     device; expert e owns rows [offsets[e], offsets[e+1])
- * w_gate, w_up [e_count, f, d]   w_dtype (MF_BF16, or MF_FP8_E4M3 codes)
- * w_down   [e_count, d, f]       w_dtype
+ * w_gate, w_up [e_count, f, d]   w_dtype (MF_BF16, or MF_FP8_E4M3 codes), packed
+ * w_down   [e_count, d, f]       w_dtype, packed (pack_weights with groups = e_count)
  * s_gate, s_up [e_count, f/128, d/128] f32, s_down [e_count, d/128, f/128] f32:
  *                                fp8 only (NULL for bf16): one scale per 128x128
  *                                block; weight value = code value * scale
@@ -216,8 +244,9 @@ int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
  * Outer Dim / Inner Dim; "LLM推理并行优化的必备知识" §1.4.
  *
  * x        [T, d]    dtype
- * w_gate_s, w_up_s [f_s, d] dtype: rows F_i of the [f, d] storage
- * w_down_s [d, f_s]  dtype: columns F_i of the [d, f] storage, contiguous
+ * w_gate_s, w_up_s [f_s, d] dtype: rows F_i of the [f, d] weight
+ * w_down_s [d, f_s]  dtype: columns F_i of the [d, f] weight
+ *                    (MF_BF16: packed by pack_weights; MF_F32: row-major as shown)
  * h_work   [T, f_s]  dtype, out: H_i
  * partial  [T, d]    f32, out: P_i, the full-shape partial sum
  * dtype MF_BF16 (MFMA, fp32 accumulation; H_i rounded to bf16; requires

@@ -69,6 +69,17 @@ def test_rmsnorm_validation(lib):
     assert lib.rmsnorm(P, P, P, 0, 64, 1e-5, BF16, N) == MF_OK
 
 
+def test_pack_validation(lib):
+    assert lib.packed_weights_bytes(2, 40, 64, BF16) == 2 * 64 * 64 * 2   # 40 rows -> 2 blocks of 32
+    assert lib.packed_weights_bytes(1, 20, 128, FP8) == 32 * 128          # 20 rows -> 2 blocks of 16
+    assert lib.packed_weights_bytes(1, 20, 100, FP8) == 0
+    assert lib.packed_weights_bytes(1, 20, 40, BF16) == 0
+    assert lib.pack_weights(N, P, 1, 32, 64, BF16, N) == MF_EINVAL
+    assert lib.pack_weights(P, P, 1, 32, 64, F32, N) == MF_EINVAL
+    assert lib.pack_weights(P, P, 1, 32, 40, BF16, N) == MF_EUNSUPPORTED
+    assert lib.pack_weights(N, N, 0, 32, 64, BF16, N) == MF_OK
+
+
 def test_route_validation(lib):
     ws = lib.moe_route_workspace_size(4, 256, 256)
     assert ws > 0 and lib.moe_route_workspace_size(4, 64, 256) == 0

@@ -68,7 +68,7 @@ def test_rmsnorm_in_place(g):
                                    (129, 2048, 100)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
-    idx, w = g.moe_route(r["x"], r["w_r"], r["bias"])
+    idx, w = g.moe_route(r["x"], g.pack_weights(r["w_r"]), r["bias"])
     torch.cuda.synchronize()
     ref_idx, ref_w, s, key, gap = oracle.route(to_f64(r["x"]), to_f64(r["w_r"]), to_f64(r["bias"]))
     n = check_route(to_i64(idx), key, gap, ref_idx)
@@ -87,7 +87,7 @@ def test_route_exact_ties_pick_lower_index(g):
     w_r = base.repeat_interleave(16, dim=0).contiguous()
     x = synth.normal((T, d), name="t.tie.x", device=DEV)
     bias = torch.zeros(E, dtype=torch.float32, device=DEV)
-    idx, w = g.moe_route(x, w_r, bias)
+    idx, w = g.moe_route(x, g.pack_weights(w_r), bias)
     torch.cuda.synchronize()
     ref_idx, *_ = oracle.route(to_f64(x), to_f64(w_r), np.zeros(E))
     got = to_i64(idx)
@@ -140,6 +140,44 @@ def test_permute_zero_tokens_writes_zero_counts(g):
     assert res.offsets.cpu().tolist() == [0] * 17
 
 
+# ------------------------------------------------------------------ packing --
+
+def _pack_reference(w: np.ndarray, fp8: bool) -> np.ndarray:
+    """The packed byte order, written out with numpy index arithmetic."""
+    G, N, K = w.shape
+    rb, cb = (16, 128) if fp8 else (32, 16)
+    nb = -(-N // rb)
+    wp = np.zeros((G, nb * rb, K), dtype=w.dtype)
+    wp[:, :N] = w
+    l = np.arange(64)
+    if fp8:
+        h = np.arange(2)
+        b = np.arange(16)
+        rows = (np.arange(nb)[:, None, None, None, None] * 16 + (l % 16)[None, None, None, :, None])
+        cols = (np.arange(K // 128)[None, :, None, None, None] * 128 + 32 * (l // 16)[None, None, None, :, None]
+                + 16 * h[None, None, :, None, None] + b[None, None, None, None, :])
+        return wp[:, rows, cols]
+    v = np.arange(8)
+    rows = np.arange(nb)[:, None, None, None] * 32 + (l % 32)[None, None, :, None]
+    cols = (np.arange(K // 16)[None, :, None, None] * 16 + 8 * (l // 32)[None, None, :, None]
+            + v[None, None, None, :])
+    return wp[:, rows, cols]
+
+
+@pytest.mark.parametrize("fp8,G,N,K", [(False, 3, 96, 64), (False, 1, 12, 256), (False, 2, 300, 48),
+                                       (True, 2, 48, 256), (True, 1, 20, 128)])
+def test_pack_weights_is_the_documented_permutation(g, fp8, G, N, K):
+    dt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    w = synth.normal((G, N, K), name="t.pack", sub=N, dtype=torch.float32, device=DEV).to(dt)
+    packed = g.pack_weights(w)
+    torch.cuda.synchronize()
+    view = np.uint8 if fp8 else np.uint16
+    src = w.cpu().view(torch.uint8 if fp8 else torch.int16).numpy().view(view)
+    ref = _pack_reference(src, fp8).reshape(-1)
+    got = packed.data.cpu().numpy().view(view)
+    assert got.shape == ref.shape and np.array_equal(got, ref)
+
+
 # ------------------------------------------------------------ grouped GEMM --
 
 def _offsets(counts):
@@ -180,7 +218,8 @@ def test_grouped_swiglu(g, wdtype, counts, d, f):
     offsets = _offsets(counts)
     h = torch.full((max_rows, f), float("nan"), dtype=torch.bfloat16, device=DEV)
     y = torch.full((max_rows, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-    g.grouped_swiglu(x_perm, offsets, W["w_gate"], W["w_up"], W["w_down"], W.get("s_gate"),
+    pw = [g.pack_weights(W[k_]) for k_ in ("w_gate", "w_up", "w_down")]
+    g.grouped_swiglu(x_perm, offsets, *pw, W.get("s_gate"),
                      W.get("s_up"), W.get("s_down"), h_work=h, y_perm=y)
     torch.cuda.synchronize()
     # rows past the last expert are never written
@@ -261,7 +300,7 @@ def test_tp_shard_bf16(g, T, d, f, p):
     total = 0
     for i in range(p):
         sg, su, sd = shard_weights(D["w_gate"], D["w_up"], D["w_down"], p, i)
-        part, h = g.tp_shard_mlp(D["x"], sg, su, sd)
+        part, h = g.tp_shard_mlp(D["x"], *(g.pack_weights(w_) for w_ in (sg, su, sd)))
         torch.cuda.synchronize()
         ref = oracle.tp_shard_mlp(xf, wg, wu, wd, p, i)
         assert_fp(f"partial {i}", to_f64(part), ref)
