@@ -299,10 +299,16 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
 
 namespace {
 
-int persistent_grid(int64_t max_rows, int e_count, int nt, int num_cus) {
-  const int64_t ub = ((max_rows + BM - 1) / BM + e_count) * static_cast<int64_t>(nt);
+// Persistent grid: at most one workgroup per CU, a multiple of 8 (the XCD
+// count), and no more than an upper bound on the tiles. With offsets each
+// group can add one partial m-tile; a single dense group (offsets == nullptr)
+// has exactly ceil(rows / BM) m-tiles.
+int persistent_grid(int64_t max_rows, int e_count, bool dense, int nt, int num_cus) {
+  const int64_t mtiles = (max_rows + BM - 1) / BM + (dense ? 0 : e_count);
+  const int64_t ub = mtiles * static_cast<int64_t>(nt);
   int64_t g = ub < num_cus ? ub : num_cus;
   g = (g + 7) & ~int64_t(7);
+  if (g > num_cus) g = num_cus & ~7;
   return static_cast<int>(g < 8 ? 8 : g);
 }
 
@@ -314,7 +320,7 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
   GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_gate),
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
                static_cast<int>(max_rows), K, N / 32, N, N, K, 0};
-  const int grid = persistent_grid(max_rows, e_count, N / 128, num_cus);
+  const int grid = persistent_grid(max_rows, e_count, offsets == nullptr, N / 128, num_cus);
   gemm_bf16_kernel<true, false><<<grid, 256, 0, s>>>(p);
 }
 
@@ -324,7 +330,7 @@ void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, i
   GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_down), nullptr,
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
                N, N, K, 0};
-  const int grid = persistent_grid(max_rows, e_count, N / 256, num_cus);
+  const int grid = persistent_grid(max_rows, e_count, offsets == nullptr, N / 256, num_cus);
   if (out_f32)
     gemm_bf16_kernel<false, true><<<grid, 256, 0, s>>>(p);
   else
@@ -340,7 +346,8 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
                reinterpret_cast<char*>(c_partials), nullptr, 1, static_cast<int>(rows), K,
                (n_valid + 31) / 32, n_valid, n_valid, K / splits,
                rows * static_cast<int64_t>(n_valid)};
-  const int gx = persistent_grid(rows, 1, 1, num_cus);
+  // splits x tiles workgroups: size x so that all of them fit in one round
+  int gx = persistent_grid(rows, 1, true, 1, num_cus / splits);
   gemm_bf16_kernel<false, true><<<dim3(gx, splits), 256, 0, s>>>(p);
 }
 

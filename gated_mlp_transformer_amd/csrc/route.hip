@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kTargetWGs = 256;   // one workgroup per CU of an MI355X
 constexpr int kTokTile = 128;     // token rows per logits tile
+constexpr int kMaxSplits = 16;
 
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
@@ -31,7 +32,7 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 int route_splits(int64_t T, int d) {
   const int64_t tiles = (T + kTokTile - 1) / kTokTile;
   int ks = 1;  // each split's K range must stay a multiple of 256
-  while ((d / 256) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs) ks *= 2;
+  while ((d / 256) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs && ks * 2 <= kMaxSplits) ks *= 2;
   return ks;
 }
 
@@ -49,15 +50,23 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   if (t >= T) return;
   const int64_t split_stride = T * E;
+  // All partial logits are loaded before any is added (independent loads in
+  // flight together), then summed in split order.
+  float part[kMaxSplits][4];
+#pragma unroll
+  for (int y = 0; y < kMaxSplits; ++y)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      part[y][c] = (y < splits && e < E) ? zp[y * split_stride + t * E + e] : 0.f;
+    }
   float s[4], kv[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
     float z = 0.f;
-    if (e < E) {
-      const float* p = zp + t * E + e;
-      for (int y = 0; y < splits; ++y) z += p[y * split_stride];
-    }
+#pragma unroll
+    for (int y = 0; y < kMaxSplits; ++y) z += part[y][c];
     s[c] = sigmoidf_(z);
     kv[c] = e < E ? s[c] + bias[e] : -__builtin_inff();
   }
