@@ -9,32 +9,44 @@
 // contiguous 1 KB block, so a wavefront loads a fragment with one fully
 // coalesced 16-byte-per-lane load, straight into registers.
 //
-// Tiling. A workgroup (256 threads, 4 waves) computes a 128-row tile against
-// 256 weight rows: 128 gate + 128 up rows (128 output columns, gate and up
-// side by side so the SiLU product stays in registers) or 256 down rows
-// (256 output columns). Each wave owns 64 weight rows (two 32-row fragments)
-// for all 128 tile rows (four 32-row sub-tiles): eight 32x32 accumulators
-// (128 fp32 per lane, kept in AGPRs, accumulated in place).
+// Tiling. A workgroup (256 threads, 4 waves) computes a tile of up to BM = 32*MT
+// rows against 256 weight rows: 128 gate + 128 up rows (128 output columns,
+// gate and up side by side so the SiLU product stays in registers) or 256 down
+// rows (256 output columns). Each wave owns 64 weight rows (two 32-row
+// fragments) for all the tile's rows: 2*MT 32x32 accumulators, kept in AGPRs
+// and accumulated in place. The grouped GEMMs use MT = 8 (256 rows, the whole
+// AGPR file): per 32-deep K stage a workgroup moves 32 KB (A 16 KB + weights
+// 16 KB) for 1024 MFMA cycles per SIMD, two thirds of the bytes per flop of
+// 128-row tiles. The router's split-K product uses MT = 4.
 //
 // Operand paths. A wave's weight fragments are private to it and come straight
-// from global memory. The A tile is shared by the four waves and goes through
-// LDS (two 16 KB buffers, 16-byte-chunk XOR swizzle chunk ^ row%8: the
-// coalesced row writes and the 32-row fragment reads are both conflict-free).
+// from global memory into registers. The A tile is shared by the four waves
+// and goes through LDS (two buffers; 64-byte rows whose 16-byte chunks are
+// XOR-swizzled so that both the row writes and the 32-row fragment reads are
+// bank-conflict free).
 //
-// Pipeline. BK = 64 per stage (four MFMA k-steps). Weights and A are loaded
-// three stages ahead; four register slots rotate through a K loop unrolled by
-// four, so every slot index is a compile-time constant and the compiler's
-// vmcnt waits cover exactly the stage consumed. A tail tile (an expert's last,
-// with fewer than 128 rows) runs a K loop instantiated for its live 32-row
-// sub-tiles only, skipping the MFMAs and LDS reads of the empty ones.
+// Pipeline. BK = 32 per stage (two MFMA k-steps). Weight fragments are loaded
+// three stages ahead into four register slots that rotate through a K loop
+// unrolled by four, so every slot index is a compile-time constant; A is
+// loaded two stages ahead into two register buffers. The loop is branch-free
+// (prefetch indices are clamped), so the compiler's vmcnt waits track exactly
+// the loads being consumed. Within a stage the instruction order is fixed
+// with scheduling groups: the stage's first-k-step fragments are read from
+// LDS, then every pair of MFMAs is followed by one second-k-step fragment read
+// and one global load, then the next stage's A tile is written to the other
+// LDS buffer between the remaining MFMAs. Spreading the loads keeps the
+// address queue from stalling the MFMA issue.
 //
 // Schedule. Group boundaries come from the device-side offsets, so no host
-// sync is needed: each workgroup turns offsets into per-group m-tile counts
-// and their prefix sum in LDS. Tiles are numbered group-major, then n-tile,
-// then m-tile, so the m-tiles that share one weight tile are consecutive.
-// The grid is persistent; workgroup b (dispatched round-robin to XCD b % 8)
-// takes tile it*G + (b%8)*(G/8) + b/8 in round it, so each XCD works on a
-// contiguous run of tiles and weight tiles are reused from its own L2.
+// sync is needed. Each workgroup computes the schedule itself: group e's
+// ceil(rows_e / 32) sub-tiles are split into ceil(sub_e / MT) near-equal
+// chunks (so an expert's last chunk is not a sliver), a tile is one chunk
+// against one n-tile, and tiles are numbered group-major, then chunk, then
+// n-tile, so the n-tiles that share one A chunk are consecutive. A tile runs a
+// K loop instantiated for its live sub-tiles only. The grid is persistent;
+// workgroup b (dispatched round-robin to XCD b % 8) takes tile
+// it*G + (b%8)*(G/8) + b/8 in round it, so each XCD works on a contiguous run
+// of tiles at a time and A chunks and weight tiles are shared through its L2.
 #include "common.h"
 #include "launch.h"
 
@@ -42,12 +54,11 @@ namespace mf {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BK = 64;
-constexpr int A_BYTES = BM * BK * 2;
+constexpr int BK = 32;         // K depth of one pipeline stage: two MFMA k-steps
+constexpr int ROWB = BK * 2;   // bytes of one A row of a stage (64)
 constexpr int MAX_GROUPS = 256;
-constexpr int PREF = 3;        // stages of loads in flight
-constexpr int SLOTS = PREF + 1;
+constexpr int SLOTS = 4;       // weight register slots
+constexpr int PREF = SLOTS - 1;  // weight stages in flight ahead of the one consumed
 constexpr int FRAG = 1024;     // bytes of one packed 32x16 weight fragment
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
@@ -69,7 +80,10 @@ struct GemmParams {
   int64_t c_split;         // elements between the C blocks of consecutive splits
 };
 
-__device__ __forceinline__ int swz(int r, int chunk) { return r * (BK * 2) + ((chunk ^ (r & 7)) << 4); }
+// A stage row is 64 bytes (four 16-byte chunks); chunk c of row r sits at
+// chunk c ^ ((r/2) % 4), so eight consecutive rows of one chunk (a fragment
+// read) and two rows of four chunks (a row write) both hit distinct banks.
+__device__ __forceinline__ int swz(int r, int chunk) { return r * ROWB + ((chunk ^ ((r >> 1) & 3)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
@@ -78,61 +92,92 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f
 
 }  // namespace
 
-// K loop of one tile for NM live 32-row sub-tiles (1..4). Branch-free: the
-// prefetch stage index is clamped (the last steps re-load the final stage),
-// so the compiler's vmcnt waits track exactly the slot being consumed.
-template <int NM>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[4][2], const char* const (&ap)[4],
-                                       const char* const (&bp)[2], char (&lds)[2][A_BYTES],
-                                       int nk, int ld_r, int ld_c, int lane) {
-  u32x4 areg[SLOTS][4];
-  u32x4 breg[SLOTS][8];  // [fragment column jn * 4 + k-step s]
+// K loop of one tile for NM live 32-row sub-tiles (1..MT). Branch-free: the
+// prefetch stage indices are clamped (the last steps re-load the final stage),
+// so the compiler's vmcnt waits track exactly the loads being consumed.
+//
+// Stage t: issue A(t+2) and the weights of t+3, run the MFMAs of t, write
+// A(t+1) (loaded during stage t-1) into the other LDS buffer, barrier.
+// Thread (ld_r, ld_c) moves chunk ld_c of rows ld_r + 64i, i < ceil(NM/2).
+template <int MT, int NM>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* const (&ap)[MT / 2],
+                                       const char* const (&bp)[2],
+                                       char (&lds)[2][MT * 32 * ROWB], int nk, int ld_r,
+                                       int ld_c, int lane) {
+  constexpr int NA = (NM + 1) / 2;  // A loads per thread per stage
+  u32x4 areg[2][NA];
+  u32x4 breg[SLOTS][4];  // [fragment column jn * 2 + k-step s]
   const int lr = lane & 31, lg = lane >> 5;
-  auto issue = [&](u32x4 (&ar)[4], u32x4 (&br)[8], int kt) {
-    const int64_t ka = static_cast<int64_t>(kt) * (BK * 2);
+  auto load_a = [&](u32x4 (&ar)[NA], int kt) {
+    const int64_t ka = static_cast<int64_t>(kt) * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ar[i] = ld16(ap[i] + ka);
-    const int64_t kb = static_cast<int64_t>(kt) * (4 * FRAG);
+    for (int i = 0; i < NA; ++i) ar[i] = ld16(ap[i] + ka);
+  };
+  auto load_b = [&](u32x4 (&br)[4], int kt) {
+    const int64_t kb = static_cast<int64_t>(kt) * (2 * FRAG);
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) br[jn * 4 + s] = ld16(bp[jn] + kb + s * FRAG);
+      for (int s = 0; s < 2; ++s) br[jn * 2 + s] = ld16(bp[jn] + kb + s * FRAG);
   };
-  auto write_a = [&](const u32x4 (&ar)[4], int buf) {
+  auto write_a = [&](const u32x4 (&ar)[NA], int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st16(&lds[buf][swz(ld_r + 32 * i, ld_c)], ar[i]);
+    for (int i = 0; i < NA; ++i) st16(&lds[buf][swz(ld_r + 64 * i, ld_c)], ar[i]);
   };
-  // k-step s reads A chunk 2s + lane/32 of each live sub-tile's rows; the next
-  // k-step's fragments are read before this k-step's MFMAs are issued.
-  auto compute = [&](const u32x4 (&br)[8], int buf) {
+  // One stage in a fixed instruction order. The k-step 0 fragments of every
+  // live sub-tile are read first. The global loads of later stages (A two
+  // stages ahead, weights three) and k-step 1's fragment reads are spread
+  // between k-step 0's MFMAs, one load per MFMA pair, so that the address
+  // queue never backs up into the MFMA issue. The next stage's A tile is
+  // written to the other LDS buffer between k-step 1's MFMAs.
+  auto stage = [&](const u32x4 (&br)[4], int buf, const u32x4 (&next_a)[NA],
+                   u32x4 (&a_dst)[NA], int kt_a, u32x4 (&b_dst)[4], int kt_b) {
+    load_a(a_dst, kt_a);
+    load_b(b_dst, kt_b);
     u32x4 af[2][NM];
 #pragma unroll
-    for (int i = 0; i < NM; ++i) af[0][i] = ld16(&lds[buf][swz(i * 32 + lr, lg)]);
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s + 1 < 4) {
+      for (int i = 0; i < NM; ++i) af[s][i] = ld16(&lds[buf][swz(i * 32 + lr, 2 * s + lg)]);
 #pragma unroll
-        for (int i = 0; i < NM; ++i)
-          af[(s + 1) & 1][i] = ld16(&lds[buf][swz(i * 32 + lr, 2 * (s + 1) + lg)]);
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        acc[i][0] = mfma32(br[s], af[s][i], acc[i][0]);
+        acc[i][1] = mfma32(br[2 + s], af[s][i], acc[i][1]);
       }
+    write_a(next_a, buf ^ 1);
+    // masks: MFMA 0x008, VMEM read 0x020, DS read 0x100, DS write 0x200
+    constexpr int NL = NA + 4;                       // global loads of the stage
+    constexpr int LEAD = NL > NM ? NL - NM : 0;      // loads that do not fit between pairs
+    __builtin_amdgcn_sched_group_barrier(0x020, LEAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
 #pragma unroll
-      for (int i = 0; i < NM; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn) acc[i][jn] = mfma32(br[jn * 4 + s], af[s & 1][i], acc[i][jn]);
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < NL - LEAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (NM - NA), 0);
   };
 
+  load_a(areg[0], 0);
+  load_a(areg[1], 1 < nk ? 1 : nk - 1);
 #pragma unroll
-  for (int s = 0; s < PREF; ++s) issue(areg[s], breg[s], s < nk ? s : nk - 1);
+  for (int s = 0; s < PREF; ++s) load_b(breg[s], s < nk ? s : nk - 1);
   write_a(areg[0], 0);
   __syncthreads();
-#define MF_GEMM_STEP(S)                                                                      \
-  {                                                                                          \
-    const int t_ = kt + (S);                                                                 \
-    issue(areg[((S) + PREF) % SLOTS], breg[((S) + PREF) % SLOTS], min(t_ + PREF, nk - 1));    \
-    compute(breg[(S)], (S) & 1);                                                             \
-    write_a(areg[((S) + 1) % SLOTS], ((S) + 1) & 1);                                         \
-    __syncthreads();                                                                         \
+#define MF_GEMM_STEP(S)                                                                    \
+  {                                                                                        \
+    const int t_ = kt + (S);                                                               \
+    stage(breg[(S)], (S) & 1, areg[((S) + 1) & 1], areg[(S) & 1], min(t_ + 2, nk - 1),      \
+          breg[((S) + PREF) % SLOTS], min(t_ + PREF, nk - 1));                             \
+    __syncthreads();                                                                       \
   }
   for (int kt = 0; kt < nk; kt += SLOTS) {
     MF_GEMM_STEP(0)
@@ -143,10 +188,11 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[4][2], const char* const (&
 #undef MF_GEMM_STEP
 }
 
-template <bool GATED, bool OUT_F32>
+template <int MT, bool GATED, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int BM = MT * 32;
   constexpr int BN_OUT = GATED ? 128 : 256;
-  __shared__ __attribute__((aligned(16))) char lds[2][A_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[2][BM * ROWB];
   __shared__ int s_tile0[MAX_GROUPS + 1];
   __shared__ int s_beg[MAX_GROUPS];
   __shared__ int s_end[MAX_GROUPS];
@@ -156,7 +202,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   const int NT = (p.nb * 32 + BN_OUT - 1) / BN_OUT;
 
   // ---- device-side schedule ---------------------------------------------
-  int mt = 0;
+  // Group e's rows form sub_e = ceil(rows_e / 32) sub-tiles, split into
+  // nch_e = ceil(sub_e / Z) near-equal chunks (the first sub_e % nch_e one
+  // sub-tile longer). A tile is one chunk against one n-tile; tiles are
+  // numbered group-major, then chunk, then n-tile.
+  constexpr int Z = MT;
+  int ntile = 0;
   if (tid < p.e_count) {
     int beg = 0, end = p.max_rows;
     if (p.offsets != nullptr) {
@@ -165,9 +216,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     }
     s_beg[tid] = beg;
     s_end[tid] = end;
-    mt = (end - beg + BM - 1) / BM;
+    ntile = ((((end - beg + 31) >> 5) + Z - 1) / Z) * NT;
   }
-  s_tile0[tid + 1] = mt;  // inclusive scan below, shifted by one
+  s_tile0[tid + 1] = ntile;  // inclusive scan below, shifted by one
   if (tid == 0) s_tile0[0] = 0;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
@@ -176,13 +227,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     s_tile0[tid + 1] += v;
     __syncthreads();
   }
-  const int total_tiles = s_tile0[p.e_count] * NT;
+  const int total_tiles = s_tile0[p.e_count];
 
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int lr = lane & 31, lg = lane >> 5;
-  const int ld_c = tid & 7;    // A: 16-byte chunk this thread moves
-  const int ld_r = tid >> 3;   // A: first row this thread moves (then +32, +64, +96)
+  const int ld_c = tid & 3;    // A: 16-byte chunk this thread moves
+  const int ld_r = tid >> 2;   // A: first row this thread moves (then +64, +128, ...)
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nk = p.kc / BK;
@@ -196,27 +247,31 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     const int L = it + xcd * (G >> 3) + slot;
     if (L >= total_tiles) break;
 
-    // group e: the last with s_tile0[e] * NT <= L
+    // group e: the last with s_tile0[e] <= L (it owns tile L)
     int lo = 0, hi = p.e_count - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_tile0[mid] * NT <= L) lo = mid; else hi = mid - 1;
+      if (s_tile0[mid] <= L) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
-    const int mt_e = s_tile0[e + 1] - s_tile0[e];
-    const int rem = L - s_tile0[e] * NT;
-    const int ni = rem / mt_e, mi = rem - ni * mt_e;
-    const int row0 = s_beg[e] + mi * BM;
-    const int rows_valid = min(BM, s_end[e] - row0);
+    const int t = L - s_tile0[e];
+    const int mi = t / NT, ni = t - mi * NT;
+    const int sub_e = (s_end[e] - s_beg[e] + 31) >> 5;
+    const int nch = (sub_e + Z - 1) / Z;
+    const int q = sub_e / nch, r = sub_e - q * nch;
+    const int z0 = mi * q + min(mi, r);            // first sub-tile of the chunk
+    const int nm = q + (mi < r ? 1 : 0);           // sub-tiles in the chunk
+    const int row0 = s_beg[e] + z0 * 32;
+    const int rows_valid = min(nm * 32, s_end[e] - row0);
     const int n0 = ni * BN_OUT;
 
     // ---- per-thread global pointers ---------------------------------------
     // A rows past the tile's valid rows re-read row0 (row m of the result
     // depends on row m of A only, and those rows are never stored).
-    const char* ap[4];
+    const char* ap[MT / 2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = ld_r + 32 * i;
+    for (int i = 0; i < MT / 2; ++i) {
+      const int r = ld_r + 64 * i;
       ap[i] = p.a + static_cast<int64_t>(row0 + (r < rows_valid ? r : 0)) * Kb + kofs_a + ld_c * 16;
     }
     const char* bp[2];
@@ -229,28 +284,39 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
                lane * 16;
     }
 
-    f32x16 acc[4][2];
+    f32x16 acc[MT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int jn = 0; jn < 2; ++jn) acc[i][jn] = f32x16{};
 
     __syncthreads();  // the previous tile's LDS reads are done
-    const int nm = (rows_valid + 31) >> 5;  // live 32-row sub-tiles
-    if (nm <= 1)
-      k_loop<1>(acc, ap, bp, lds, nk, ld_r, ld_c, lane);
-    else if (nm == 2)
-      k_loop<2>(acc, ap, bp, lds, nk, ld_r, ld_c, lane);
-    else if (nm == 3)
-      k_loop<3>(acc, ap, bp, lds, nk, ld_r, ld_c, lane);
-    else
-      k_loop<4>(acc, ap, bp, lds, nk, ld_r, ld_c, lane);
+    if constexpr (MT == 8) {
+      switch (nm) {
+        case 1: k_loop<MT, 1>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 4: k_loop<MT, 4>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 5: k_loop<MT, 5>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 6: k_loop<MT, 6>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 7: k_loop<MT, 7>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 8>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+      }
+    } else {
+      static_assert(MT == 4, "MT is 4 or 8");
+      switch (nm) {
+        case 1: k_loop<MT, 1>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 4>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+      }
+    }
 
     // ---- epilogue ----------------------------------------------------------
     // Lane l holds, for row lr of sub-tile i, output columns
     // 8q + 4(l/32) + 0..3 (q = 0..3) of each 32-column fragment column jn.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MT; ++i) {
       const int m = i * 32 + lr;
       if (m >= rows_valid) continue;
       const int64_t grow = row0 + m;
@@ -299,12 +365,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
 
 namespace {
 
+constexpr int MT_GROUPED = 8;  // 256-row tiles for the grouped and dense GEMMs
+constexpr int MT_SPLITK = 4;   // 128-row tiles for the router's split-K product
+
 // Persistent grid: at most one workgroup per CU, a multiple of 8 (the XCD
 // count), and no more than an upper bound on the tiles. With offsets each
 // group can add one partial m-tile; a single dense group (offsets == nullptr)
 // has exactly ceil(rows / BM) m-tiles.
-int persistent_grid(int64_t max_rows, int e_count, bool dense, int nt, int num_cus) {
-  const int64_t mtiles = (max_rows + BM - 1) / BM + (dense ? 0 : e_count);
+int persistent_grid(int64_t max_rows, int bm, int e_count, bool dense, int nt, int num_cus) {
+  const int64_t mtiles = (max_rows + bm - 1) / bm + (dense ? 0 : e_count);
   const int64_t ub = mtiles * static_cast<int64_t>(nt);
   int64_t g = ub < num_cus ? ub : num_cus;
   g = (g + 7) & ~int64_t(7);
@@ -320,8 +389,9 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
   GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_gate),
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
                static_cast<int>(max_rows), K, N / 32, N, N, K, 0};
-  const int grid = persistent_grid(max_rows, e_count, offsets == nullptr, N / 128, num_cus);
-  gemm_bf16_kernel<true, false><<<grid, 256, 0, s>>>(p);
+  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
+                                   N / 128, num_cus);
+  gemm_bf16_kernel<MT_GROUPED, true, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
@@ -330,11 +400,12 @@ void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, i
   GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_down), nullptr,
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
                N, N, K, 0};
-  const int grid = persistent_grid(max_rows, e_count, offsets == nullptr, N / 256, num_cus);
+  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
+                                   N / 256, num_cus);
   if (out_f32)
-    gemm_bf16_kernel<false, true><<<grid, 256, 0, s>>>(p);
+    gemm_bf16_kernel<MT_GROUPED, false, true><<<grid, 256, 0, s>>>(p);
   else
-    gemm_bf16_kernel<false, false><<<grid, 256, 0, s>>>(p);
+    gemm_bf16_kernel<MT_GROUPED, false, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b, int n_valid,
@@ -347,8 +418,8 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
                (n_valid + 31) / 32, n_valid, n_valid, K / splits,
                rows * static_cast<int64_t>(n_valid)};
   // splits x tiles workgroups: size x so that all of them fit in one round
-  int gx = persistent_grid(rows, 1, true, 1, num_cus / splits);
-  gemm_bf16_kernel<false, true><<<dim3(gx, splits), 256, 0, s>>>(p);
+  int gx = persistent_grid(rows, MT_SPLITK * 32, 1, true, 1, num_cus / splits);
+  gemm_bf16_kernel<MT_SPLITK, false, true><<<dim3(gx, splits), 256, 0, s>>>(p);
 }
 
 }  // namespace mf
