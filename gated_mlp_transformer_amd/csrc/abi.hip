@@ -154,7 +154,7 @@ void enqueue_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count
                                 num_cus(), s);
   else
     mf::launch_gemm_gateup_fp8(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
-                               s_up, h, s);
+                               s_up, h, num_cus(), s);
 }
 
 void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t max_rows,
@@ -164,7 +164,8 @@ void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_
     mf::launch_gemm_down_bf16(h, offsets, e_count, max_rows, f, d, w_down, y, false, num_cus(),
                               s);
   else
-    mf::launch_gemm_down_fp8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, s);
+    mf::launch_gemm_down_fp8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, num_cus(),
+                             s);
 }
 
 }  // namespace

@@ -7,9 +7,10 @@
 // with W[n, k] = code[n, k] * scale[n/128, k/128].
 //
 // Shaped for decode, where an expert holds a handful of rows and the kernel
-// streams weights from HBM once: one workgroup per (expert, 256 output
-// columns), each wave 64 columns as four 16-row weight sub-tiles (eight for
-// gate + up). The weight sub-tile is the MFMA's first operand; the expert's
+// streams weights from HBM once. A work item is one expert against NTW output
+// columns (256 for gate/up, 512 for down); each wave owns a quarter of them as
+// eight 16-row weight sub-tiles (four gate + four up, or eight down), so that
+// a wave's weight loads per 128-deep slab (16 KB) dwarf its A loads (4 KB). The weight sub-tile is the MFMA's first operand; the expert's
 // rows (up to 16 per pass, zero-padded) are the second. Every lane loads 32
 // weight bytes of a 128-deep slab per sub-tile (row l%16, bytes 32(l/16) +
 // 0..31), from weights packed so that each of its two 16-byte loads is one
@@ -22,6 +23,14 @@
 // The next slab's loads are issued before the current slab is consumed.
 // Experts with more than 16 rows are processed 16 rows at a time (the weights
 // are re-read per pass; decode shapes need one pass).
+//
+// Schedule. Items of experts without rows do not exist. The grid is persistent
+// (one workgroup per CU) and workgroup b takes items b, b + G, b + 2G, ...:
+// with equal items, a few hundred of them over G workgroups leave the last
+// round nearly full, where one workgroup per item would leave a partial
+// round of whole workgroups idle. Each workgroup derives the item list from
+// the device-side offsets (an LDS prefix sum over experts), so no host sync is
+// needed.
 #include "common.h"
 #include "launch.h"
 
@@ -29,8 +38,9 @@ namespace mf {
 
 namespace {
 
-constexpr int NTW = 256;  // output columns per workgroup
+constexpr int R = 8;      // 16-row weight sub-tiles per wave
 constexpr int SLAB = 128; // K depth per scale block
+constexpr int MAX_GROUPS = 256;
 
 struct Fp8Params {
   const char* a;           // [max_rows, K] bf16
@@ -55,114 +65,160 @@ struct SlabRegs {
 
 template <bool GATED>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
-  constexpr int R = GATED ? 8 : 4;  // 16-row weight sub-tiles per wave
-  const int ntw = p.N / NTW;
-  const int e = blockIdx.x / ntw;
-  const int nt = blockIdx.x - e * ntw;
-  const int beg = clampi(p.offsets[e], 0, p.max_rows);
-  const int end = clampi(p.offsets[e + 1], beg, p.max_rows);
-  if (end <= beg) return;
+  constexpr int NTW = GATED ? 256 : 512;  // output columns per work item
+  constexpr int QH = GATED ? R / 2 : R;   // sub-tiles per weight matrix per wave
+  __shared__ int s_item0[MAX_GROUPS + 1];
+  __shared__ int s_beg[MAX_GROUPS];
+  __shared__ int s_end[MAX_GROUPS];
+  const int tid = threadIdx.x;
+  const int ntw = (p.N + NTW - 1) / NTW;  // items per active expert (the last may be partial)
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
+  // ---- device-side item list: prefix over experts of ntw items per active expert
+  int items = 0;
+  if (tid < p.e_count) {
+    const int beg = clampi(p.offsets[tid], 0, p.max_rows);
+    const int end = clampi(p.offsets[tid + 1], beg, p.max_rows);
+    s_beg[tid] = beg;
+    s_end[tid] = end;
+    items = end > beg ? ntw : 0;
+  }
+  s_item0[tid + 1] = items;  // inclusive scan below, shifted by one
+  if (tid == 0) s_item0[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? s_item0[tid + 1 - off] : 0;
+    __syncthreads();
+    s_item0[tid + 1] += v;
+    __syncthreads();
+  }
+  const int total_items = s_item0[p.e_count];
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n0w = nt * NTW + wave * 64;
   const int kslabs = p.K / SLAB;
   const int64_t K = p.K;
 
-  // Packed fp8 weights: 16-row x 128-column blocks of 2 KB, [half][lane][16 B];
-  // lane l's two 16-byte loads of a block are row l%16, bytes 32(l/16) + 0..31
-  // of the block's 128-byte slab, each load one contiguous 1 KB across lanes.
-  const int kblocks = p.K / SLAB;
-  const uint8_t* wp[R];
-#pragma unroll
-  for (int q = 0; q < R; ++q) {
-    const uint8_t* base = (GATED && q >= 4) ? p.b1 : p.b0;
-    const int nb = (n0w >> 4) + (q & 3);
-    wp[q] = base + ((static_cast<int64_t>(e) * (p.N / 16) + nb) * kblocks) * 2048 +
-            lane * 16;
-  }
-  const int64_t sbase = (static_cast<int64_t>(e) * (p.N / SLAB) + n0w / SLAB) * kslabs;
-  const float* sp0 = p.s0 + sbase;
-  const float* sp1 = GATED ? p.s1 + sbase : nullptr;
-
-  for (int m0 = beg; m0 < end; m0 += 16) {
-    const int rows_valid = min(16, end - m0);
-    const bool arow_ok = lr < rows_valid;
-    const char* ap = p.a + static_cast<int64_t>(m0 + (arow_ok ? lr : 0)) * K * 2 + 64 * lg;
-
-    f32x4 acc[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    SlabRegs<R> cur, nxt;
-    auto load = [&](SlabRegs<R>& s, int kb) {
-      const int64_t kofs = static_cast<int64_t>(kb) * SLAB;
-      const int64_t bofs = static_cast<int64_t>(kb) * 2048;
-#pragma unroll
-      for (int q = 0; q < R; ++q) {
-        s.b[q][0] = ld16(wp[q] + bofs);
-        s.b[q][1] = ld16(wp[q] + bofs + 1024);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        s.a[c] = arow_ok ? ld16(ap + kofs * 2 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-    };
-
-    load(cur, 0);
-    for (int kb = 0; kb < kslabs; ++kb) {
-      if (kb + 1 < kslabs) load(nxt, kb + 1);
-      const float sc0 = sp0[kb];
-      const float sc1 = GATED ? sp1[kb] : 0.f;
-#pragma unroll
-      for (int q = 0; q < R; ++q) {
-        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4& w = cur.b[q][c >> 1];
-          const u32x2 lo = fp8x4_to_bf16x4(w[(c & 1) * 2]);
-          const u32x2 hi = fp8x4_to_bf16x4(w[(c & 1) * 2 + 1]);
-          sa = mfma16x16x32(u32x4{lo[0], lo[1], hi[0], hi[1]}, cur.a[c], sa);
-        }
-        const float sc = (GATED && q >= 4) ? sc1 : sc0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(sc, sa[r], acc[q][r]);
-      }
-      cur = nxt;
+  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+    // expert e: the last with s_item0[e] <= item (it owns the item)
+    int lo = 0, hi = p.e_count - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_item0[mid] <= item) lo = mid; else hi = mid - 1;
     }
+    const int e = lo;
+    const int nt = item - s_item0[e];
+    const int beg = s_beg[e], end = s_end[e];
+    const int n0w = nt * NTW + wave * (16 * QH);
+    // N is a multiple of 16 * QH, so a wave's columns are all in range or all
+    // past N; a wave past N has nothing to do for this item (there is no
+    // workgroup barrier inside the item loop).
+    if (n0w >= p.N) continue;
 
-    // lane holds output columns 4*lg..4*lg+3 of sub-tile q for row lr.
-    if (arow_ok) {
-      const int64_t grow = m0 + lr;
+    // Packed fp8 weights: 16-row x 128-column blocks of 2 KB, [half][lane][16 B];
+    // lane l's two 16-byte loads of a block are row l%16, bytes 32(l/16) + 0..31
+    // of the block's 128-byte slab, each load one contiguous 1 KB across lanes.
+    const uint8_t* wp[R];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0w + 16 * q + 4 * lg;
-        float h[4];
+    for (int q = 0; q < R; ++q) {
+      const uint8_t* base = (GATED && q >= QH) ? p.b1 : p.b0;
+      const int nb = (n0w >> 4) + (q % QH);
+      wp[q] = base + ((static_cast<int64_t>(e) * (p.N / 16) + nb) * kslabs) * 2048 + lane * 16;
+    }
+    const int64_t sbase = (static_cast<int64_t>(e) * (p.N / SLAB) + n0w / SLAB) * kslabs;
+    const float* sp0 = p.s0 + sbase;
+    const float* sp1 = GATED ? p.s1 + sbase : nullptr;
+
+    for (int m0 = beg; m0 < end; m0 += 16) {
+      const int rows_valid = min(16, end - m0);
+      const bool arow_ok = lr < rows_valid;
+      const char* ap = p.a + static_cast<int64_t>(m0 + (arow_ok ? lr : 0)) * K * 2 + 64 * lg;
+
+      f32x4 acc[R];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = GATED ? siluf_(acc[q][r]) * acc[q + (GATED ? 4 : 0)][r] : acc[q][r];
-        *reinterpret_cast<u32x2*>(p.c + (grow * p.N + col) * 2) =
-            u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+      for (int q = 0; q < R; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      SlabRegs<R> cur, nxt;
+      auto load = [&](SlabRegs<R>& s, int kb) {
+        const int64_t kofs = static_cast<int64_t>(kb) * SLAB;
+        const int64_t bofs = static_cast<int64_t>(kb) * 2048;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          s.b[q][0] = ld16(wp[q] + bofs);
+          s.b[q][1] = ld16(wp[q] + bofs + 1024);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          s.a[c] = arow_ok ? ld16(ap + kofs * 2 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      };
+
+      load(cur, 0);
+      for (int kb = 0; kb < kslabs; ++kb) {
+        if (kb + 1 < kslabs) load(nxt, kb + 1);
+        const float sc0 = sp0[kb];
+        const float sc1 = GATED ? sp1[kb] : 0.f;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4& w = cur.b[q][c >> 1];
+            const u32x2 lo2 = fp8x4_to_bf16x4(w[(c & 1) * 2]);
+            const u32x2 hi2 = fp8x4_to_bf16x4(w[(c & 1) * 2 + 1]);
+            sa = mfma16x16x32(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, cur.a[c], sa);
+          }
+          const float sc = (GATED && q >= QH) ? sc1 : sc0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(sc, sa[r], acc[q][r]);
+        }
+        cur = nxt;
+      }
+
+      // lane holds output columns 4*lg..4*lg+3 of sub-tile q for row lr.
+      if (arow_ok) {
+        const int64_t grow = m0 + lr;
+#pragma unroll
+        for (int q = 0; q < QH; ++q) {
+          const int col = n0w + 16 * q + 4 * lg;
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            h[r] = GATED ? siluf_(acc[q][r]) * acc[q + (GATED ? QH : 0)][r] : acc[q][r];
+          *reinterpret_cast<u32x2*>(p.c + (grow * p.N + col) * 2) =
+              u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
+        }
       }
     }
   }
 }
 
+namespace {
+
+// One persistent workgroup per CU, but no more than there can be items.
+unsigned fp8_grid(int e_count, int N, int ntw, int num_cus) {
+  const int64_t ub = static_cast<int64_t>(e_count) * ((N + ntw - 1) / ntw);
+  const int64_t g = ub < num_cus ? ub : num_cus;
+  return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
 void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                             int K, int N, const void* w_gate, const void* w_up,
-                            const float* s_gate, const float* s_up, void* h, hipStream_t s) {
+                            const float* s_gate, const float* s_up, void* h, int num_cus,
+                            hipStream_t s) {
   Fp8Params p{static_cast<const char*>(a), static_cast<const uint8_t*>(w_gate),
               static_cast<const uint8_t*>(w_up), s_gate, s_up, static_cast<char*>(h), offsets,
               e_count, static_cast<int>(max_rows), K, N};
-  gemm_fp8_kernel<true><<<dim3(static_cast<unsigned>(e_count * (N / NTW))), 256, 0, s>>>(p);
+  gemm_fp8_kernel<true><<<dim3(fp8_grid(e_count, N, 256, num_cus)), 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                           int K, int N, const void* w_down, const float* s_down, void* y,
-                          hipStream_t s) {
+                          int num_cus, hipStream_t s) {
   Fp8Params p{static_cast<const char*>(a), static_cast<const uint8_t*>(w_down), nullptr, s_down,
               nullptr, static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N};
-  gemm_fp8_kernel<false><<<dim3(static_cast<unsigned>(e_count * (N / NTW))), 256, 0, s>>>(p);
+  gemm_fp8_kernel<false><<<dim3(fp8_grid(e_count, N, 512, num_cus)), 256, 0, s>>>(p);
 }
 
 }  // namespace mf

@@ -46,10 +46,10 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
 void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count,
                             int64_t max_rows, int K, int N, const void* w_gate,
                             const void* w_up, const float* s_gate, const float* s_up,
-                            void* h, hipStream_t s);
+                            void* h, int num_cus, hipStream_t s);
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
                           int64_t max_rows, int K, int N, const void* w_down,
-                          const float* s_down, void* y, hipStream_t s);
+                          const float* s_down, void* y, int num_cus, hipStream_t s);
 
 void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w,
                     int64_t T, int k, int d, int64_t max_rows, void* out,
