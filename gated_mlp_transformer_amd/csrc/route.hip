@@ -12,6 +12,10 @@
 //     order: deterministic), applies the sigmoid and the bias, and picks the
 //     top 8 by eight rounds of a wave-wide arg-max on (key descending, id
 //     ascending); the ids are emitted ascending with w = s / sum(s).
+//     The arg-max runs on one 64-bit value per lane, the key mapped to an
+//     order-preserving unsigned integer in the high word and 255 - id in the
+//     low word, reduced across the wave with DPP lane moves (register speed,
+//     no LDS round trips) and read back from the last lane.
 #include "common.h"
 #include "launch.h"
 
@@ -23,8 +27,40 @@ constexpr int kTargetWGs = 256;   // one workgroup per CU of an MI355X
 constexpr int kTokTile = 128;     // token rows per logits tile
 constexpr int kMaxSplits = 16;
 
-__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
+// Unsigned integer with the same order as the float (finite values and
+// infinities; 0 is below every such value).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// One step of a wave-wide max of the pair (hi, lo), compared as hi:lo: every
+// lane takes the larger of its pair and the pair DPP moves to it. Lanes in
+// rows outside ROW_MASK receive their own pair (the DPP "old" value).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ph = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROW_MASK, 0xF, false));
+  const uint32_t pl = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROW_MASK, 0xF, false));
+  const bool take = ph > hi || (ph == hi && pl > lo);
+  hi = take ? ph : hi;
+  lo = take ? pl : lo;
+}
+
+// Wave-wide max of (hi, lo); the result is uniform. After the two quad
+// permutations and the two mirrors every lane holds its 16-lane row's max;
+// row_bcast15 folds row 0 into row 1 and row 2 into row 3, row_bcast31 folds
+// lane 31 into row 3, so lane 63 holds the maximum of all 64 lanes.
+__device__ __forceinline__ void wave_max64(uint32_t& hi, uint32_t& lo) {
+  max_step<0xB1, 0xF>(hi, lo);   // quad_perm [1,0,3,2]
+  max_step<0x4E, 0xF>(hi, lo);   // quad_perm [2,3,0,1]
+  max_step<0x141, 0xF>(hi, lo);  // row_half_mirror
+  max_step<0x140, 0xF>(hi, lo);  // row_mirror
+  max_step<0x142, 0xA>(hi, lo);  // row_bcast15 into rows 1 and 3
+  max_step<0x143, 0xC>(hi, lo);  // row_bcast31 into rows 2 and 3
+  hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
+  lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
 }
 
 }  // namespace
@@ -60,7 +96,10 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
       const int e = lane + 64 * c;
       part[y][c] = (y < splits && e < E) ? zp[y * split_stride + t * E + e] : 0.f;
     }
-  float s[4], kv[4];
+  // candidates of this lane: experts lane + 64c; key order in the high word,
+  // 255 - id in the low word (E <= 256), invalid experts at the bottom
+  float s[4];
+  uint32_t kh[4], kl[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
@@ -68,39 +107,33 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 #pragma unroll
     for (int y = 0; y < kMaxSplits; ++y) z += part[y][c];
     s[c] = sigmoidf_(z);
-    kv[c] = e < E ? s[c] + bias[e] : -__builtin_inff();
+    kh[c] = e < E ? order_key(s[c] + bias[e]) : 0u;
+    kl[c] = static_cast<uint32_t>(255 - e);
   }
   int sel[8];
   float ssel[8];
 #pragma unroll
   for (int round = 0; round < 8; ++round) {
-    float bk = -__builtin_inff(), bs = 0.f;
-    int bi = 0x7fffffff;
+    uint32_t bh = kh[0], bl = kl[0];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      if (better(kv[c], e, bk, bi)) {
-        bk = kv[c];
-        bi = e;
-        bs = s[c];
+    for (int c = 1; c < 4; ++c) {
+      if (kh[c] > bh || (kh[c] == bh && kl[c] > bl)) {
+        bh = kh[c];
+        bl = kl[c];
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ok = __shfl_xor(bk, m, kWave);
-      const int oi = __shfl_xor(bi, m, kWave);
-      const float os = __shfl_xor(bs, m, kWave);
-      if (better(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-        bs = os;
-      }
-    }
-    sel[round] = bi;
-    ssel[round] = bs;
+    wave_max64(bh, bl);
+    const int id = 255 - static_cast<int>(bl);  // uniform
+    const int cw = id >> 6, lw = id & 63;
+    const float sv = cw == 0 ? s[0] : cw == 1 ? s[1] : cw == 2 ? s[2] : s[3];
+    sel[round] = id;
+    ssel[round] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), lw));
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (lane + 64 * c == bi) kv[c] = -__builtin_inff();  // the owner lane retires the winner
+      if (c == cw && lane == lw) {  // the owner lane retires the winner
+        kh[c] = 0u;
+        kl[c] = 0u;
+      }
   }
   // ids ascending (I is a set), scores carried along
 #pragma unroll
