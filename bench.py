@@ -67,8 +67,10 @@ def moe_work(T, d, f, E, k, S, active, ec, welt):
     return {
         "rmsnorm": dict(bytes=2 * T * d * 2 + d * 2),
         "moe_route": dict(bytes=T * d * 2 + E * d * 2 + E * 4 + T * k * 8, flops=2 * T * d * E),
-        "moe_permute": dict(bytes=T * k * 8 + S * 4 + (ec + 1) * 8 + 2 * S * d * 2),
-        "grouped_gate_up": dict(bytes=active * (2 * f * d * welt + 2 * sc) + S * d * 2 + S * f * 2,
+        # indices only: the rows V[src_token] are gathered by the gate/up GEMM's A load
+        "moe_permute": dict(bytes=T * k * 8 + S * 4 + (ec + 1) * 8),
+        "grouped_gate_up": dict(bytes=active * (2 * f * d * welt + 2 * sc) + S * d * 2 + S * f * 2
+                                + S * 4,
                                 flops=4 * S * d * f),
         "grouped_down": dict(bytes=active * (d * f * welt + sc) + S * f * 2 + S * d * 2,
                              flops=2 * S * f * d),

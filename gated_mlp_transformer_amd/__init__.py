@@ -201,11 +201,25 @@ def moe_permute(topk_idx: torch.Tensor, e_begin: int, e_count: int,
     return PermuteResult(counts, offsets, src_token, inv_pos, x_perm)
 
 
+def _grouped_rows(x: torch.Tensor, row_index, name: str):
+    """(max_rows, src_rows) of a grouped call: x is X_perm, or with row_index
+    the un-permuted rows that row_index (moe_permute's src_token) gathers."""
+    if row_index is None:
+        return x.shape[0], 0
+    if row_index.dtype != torch.int32 or row_index.dim() != 1:
+        raise ValueError(f"{name}: row_index must be a 1-D int32 tensor")
+    return row_index.numel(), x.shape[0]
+
+
 def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
                    w_up: torch.Tensor, w_down: torch.Tensor, s_gate=None, s_up=None,
-                   s_down=None, *, h_work=None, y_perm=None, stream=None):
-    """Grouped expert gated MLPs over expert-contiguous rows. Returns (y_perm, h_work)."""
-    max_rows, d = x_perm.shape
+                   s_down=None, *, row_index=None, h_work=None, y_perm=None, stream=None):
+    """Grouped expert gated MLPs over expert-contiguous rows. Returns (y_perm, h_work).
+
+    With ``row_index`` (moe_permute's src_token), ``x_perm`` is the un-permuted
+    input and row r of the grouped input is ``x_perm[row_index[r]]``."""
+    max_rows, src_rows = _grouped_rows(x_perm, row_index, "grouped_swiglu")
+    d = x_perm.shape[1]
     w_gate, w_up, w_down = (_pw(w, "grouped_swiglu") for w in (w_gate, w_up, w_down))
     e_count, f, d2 = w_gate.groups, w_gate.N, w_gate.K
     if (d2 != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d)
@@ -218,9 +232,10 @@ def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Te
         h_work = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=x_perm.device)
-    _dev(x_perm, offsets, s_gate, s_up, s_down, h_work, y_perm)
+    _dev(x_perm, row_index, offsets, s_gate, s_up, s_down, h_work, y_perm)
     _ok("grouped_swiglu", _lib.load().grouped_swiglu(
-        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate.data), _p(w_up.data),
+        _p(x_perm), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
+        _p(w_gate.data), _p(w_up.data),
         _p(w_down.data), wdt,
         _p(s_gate), _p(s_up), _p(s_down), _p(h_work), _p(y_perm), _s(stream)))
     return y_perm, h_work
@@ -236,10 +251,13 @@ def _grouped_dtype(w_gate: PackedWeights, *rest: PackedWeights) -> int:
 
 
 def grouped_gate_up(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Tensor,
-                    w_up: torch.Tensor, s_gate=None, s_up=None, *, h_out=None,
+                    w_up: torch.Tensor, s_gate=None, s_up=None, *, row_index=None, h_out=None,
                     stream=None) -> torch.Tensor:
-    """H = SiLU(X_perm W_gate_e) * (X_perm W_up_e) per expert segment. Returns h_out."""
-    max_rows, d = x_perm.shape
+    """H = SiLU(X_perm W_gate_e) * (X_perm W_up_e) per expert segment. Returns h_out.
+
+    ``row_index`` as in grouped_swiglu (the gather fused into the A load)."""
+    max_rows, src_rows = _grouped_rows(x_perm, row_index, "grouped_gate_up")
+    d = x_perm.shape[1]
     w_gate, w_up = _pw(w_gate, "grouped_gate_up"), _pw(w_up, "grouped_gate_up")
     e_count, f = w_gate.groups, w_gate.N
     if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
@@ -247,10 +265,10 @@ def grouped_gate_up(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.T
     wdt = _grouped_dtype(w_gate, w_up)
     if h_out is None:
         h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
-    _dev(x_perm, offsets, s_gate, s_up, h_out)
+    _dev(x_perm, row_index, offsets, s_gate, s_up, h_out)
     _ok("grouped_gate_up", _lib.load().grouped_gate_up(
-        _p(x_perm), _p(offsets), e_count, max_rows, d, f, _p(w_gate.data), _p(w_up.data), wdt,
-        _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
+        _p(x_perm), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
+        _p(w_gate.data), _p(w_up.data), wdt, _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
     return h_out
 
 
@@ -274,16 +292,18 @@ def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s
 
 def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor,
                 out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
-    """out[t] = sum_j topk_w[t,j] * y_perm[inv_pos[t,j]] over local slots."""
+                residual: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = sum_j topk_w[t,j] * y_perm[inv_pos[t,j]] over local slots (+ residual[t])."""
     T, k = inv_pos.shape
     max_rows, d = y_perm.shape
     if out is None:
         out = torch.empty((T, d), dtype=out_dtype, device=y_perm.device)
-    _dev(y_perm, inv_pos, topk_w, out)
+    if residual is not None and (residual.shape != out.shape or residual.dtype != out.dtype):
+        raise ValueError("moe_combine: residual must match out in shape and dtype")
+    _dev(y_perm, inv_pos, topk_w, residual, out)
     _ok("moe_combine", _lib.load().moe_combine(_p(y_perm), _p(inv_pos), _p(topk_w), T, k, d,
-                                               max_rows, _p(out), _dtype_code(out.dtype),
-                                               _s(stream)))
+                                               max_rows, _p(residual), _p(out),
+                                               _dtype_code(out.dtype), _s(stream)))
     return out
 
 
@@ -324,9 +344,11 @@ class MoEFFNLayer:
     ``forward`` enqueues rmsnorm -> moe_route -> moe_permute -> grouped_gate_up ->
     grouped_down (the two halves of grouped_swiglu) -> moe_combine on the
     current stream and returns the [T, d] output (the partial sum over this
-    rank's experts [e_begin, e_begin + e_count)). ``marks``, if given, is a
-    list of 7 events recorded before each of the six stages and after the last
-    (rmsnorm's slot is recorded even when the layer has no norm).
+    rank's experts [e_begin, e_begin + e_count), plus ``residual`` if given).
+    The permutation runs indices-only: the gate/up GEMM gathers its rows
+    V[src_token] inside its A load, so X_perm is never written. ``marks``, if
+    given, is a list of 7 events recorded before each of the six stages and
+    after the last (rmsnorm's slot is recorded even when the layer has no norm).
     """
 
     STAGES = ("rmsnorm", "moe_route", "moe_permute", "grouped_gate_up", "grouped_down",
@@ -357,12 +379,12 @@ class MoEFFNLayer:
                                      dtype=torch.uint8, device=dev)
         self.route_ws = torch.empty(max(1, moe_route_workspace_size(T, d, self.w_r.N)),
                                     dtype=torch.uint8, device=dev)
-        self.x_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.h = torch.empty((rows, f), dtype=bf, device=dev)
         self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
 
-    def forward(self, x: torch.Tensor, stream=None, marks=None) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, stream=None, marks=None,
+                residual: Optional[torch.Tensor] = None) -> torch.Tensor:
         s = torch.cuda.current_stream() if stream is None else stream
 
         def mark(i):
@@ -376,16 +398,17 @@ class MoEFFNLayer:
         mark(1)
         moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, self.route_ws, stream=s)
         mark(2)
-        moe_permute(self.idx, self.e_begin, self.e_count, v, x_perm=self.x_perm,
-                    counts=self.counts, offsets=self.offsets, src_token=self.src_token,
-                    inv_pos=self.inv_pos, workspace=self.workspace, stream=s)
+        moe_permute(self.idx, self.e_begin, self.e_count, None, counts=self.counts,
+                    offsets=self.offsets, src_token=self.src_token, inv_pos=self.inv_pos,
+                    workspace=self.workspace, stream=s)
         mark(3)
-        grouped_gate_up(self.x_perm, self.offsets, self.w[0], self.w[1], self.s[0], self.s[1],
-                        h_out=self.h, stream=s)
+        grouped_gate_up(v, self.offsets, self.w[0], self.w[1], self.s[0], self.s[1],
+                        row_index=self.src_token, h_out=self.h, stream=s)
         mark(4)
         grouped_down(self.h, self.offsets, self.w[2], self.s[2], y_perm=self.y_perm, stream=s)
         mark(5)
-        out = moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out, stream=s)
+        out = moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out,
+                          residual=residual, stream=s)
         mark(6)
         return out
 

@@ -29,15 +29,16 @@ _SIGNATURES = {
     "moe_permute": (_i32, [_c_void_p, _i64, _i32, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size,
                            _c_void_p]),
-    "grouped_swiglu": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
-                              _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
-                              _c_void_p, _c_void_p, _c_void_p]),
-    "grouped_gate_up": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
-                               _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_swiglu": (_i32, [_c_void_p, _c_void_p, _i64, _c_void_p, _i32, _i64, _i32, _i32,
+                              _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_gate_up": (_i32, [_c_void_p, _c_void_p, _i64, _c_void_p, _i32, _i64, _i32, _i32,
+                               _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p]),
     "grouped_down": (_i32, [_c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _i32,
                             _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
-                           _i32, _c_void_p]),
+                           _c_void_p, _i32, _c_void_p]),
     "tp_shard_mlp": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
                             _c_void_p, _c_void_p, _c_void_p]),
 }

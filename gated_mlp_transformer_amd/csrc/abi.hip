@@ -127,10 +127,12 @@ namespace {
 // may proceed, a status otherwise (MF_OK with *empty set for max_rows == 0).
 int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_t max_rows,
                   int32_t d, int32_t f, int32_t w_dtype, const void* w0, const void* w1,
-                  const float* s0, const float* s1, const void* out, bool* empty) {
+                  const float* s0, const float* s1, const void* out, bool* empty,
+                  const int32_t* row_index = nullptr, int64_t src_rows = 0) {
   *empty = false;
   if (!offsets || !w0 || !w1) return MF_EINVAL;
   if (e_count < 1 || max_rows < 0 || d <= 0 || f <= 0) return MF_EINVAL;
+  if (row_index && (src_rows < 1 || src_rows > kI32Max)) return MF_EINVAL;
   if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
   if (w_dtype == MF_FP8_E4M3 && (!s0 || !s1)) return MF_EINVAL;
   if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
@@ -145,16 +147,16 @@ int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_
   return MF_OK;
 }
 
-void enqueue_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count,
-                     int64_t max_rows, int32_t d, int32_t f, const void* w_gate, const void* w_up,
-                     int32_t w_dtype, const float* s_gate, const float* s_up, void* h,
-                     hipStream_t s) {
+void enqueue_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
+                     const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
+                     int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+                     const float* s_gate, const float* s_up, void* h, hipStream_t s) {
   if (w_dtype == MF_BF16)
-    mf::launch_gemm_gateup_bf16(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, h,
-                                num_cus(), s);
+    mf::launch_gemm_gateup_bf16(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
+                                w_up, h, num_cus(), s);
   else
-    mf::launch_gemm_gateup_fp8(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
-                               s_up, h, num_cus(), s);
+    mf::launch_gemm_gateup_fp8(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
+                               w_up, s_gate, s_up, h, num_cus(), s);
 }
 
 void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t max_rows,
@@ -170,15 +172,16 @@ void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_
 
 }  // namespace
 
-int grouped_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count, int64_t max_rows,
-                    int32_t d, int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+int grouped_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
+                    const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
+                    int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
                     const float* s_gate, const float* s_up, void* h_out, void* stream) {
   bool empty;
-  const int st = check_grouped(x_perm, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up,
-                               s_gate, s_up, h_out, &empty);
+  const int st = check_grouped(x, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up,
+                               s_gate, s_up, h_out, &empty, row_index, src_rows);
   if (st != MF_OK || empty) return st;
-  enqueue_gate_up(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, w_dtype, s_gate, s_up,
-                  h_out, S(stream));
+  enqueue_gate_up(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate, w_up,
+                  w_dtype, s_gate, s_up, h_out, S(stream));
   return finish();
 }
 
@@ -193,35 +196,36 @@ int grouped_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t
   return finish();
 }
 
-int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count, int64_t max_rows,
-                   int32_t d, int32_t f, const void* w_gate, const void* w_up, const void* w_down,
+int grouped_swiglu(const void* x, const int32_t* row_index, int64_t src_rows,
+                   const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
+                   int32_t f, const void* w_gate, const void* w_up, const void* w_down,
                    int32_t w_dtype, const float* s_gate, const float* s_up, const float* s_down,
                    void* h_work, void* y_perm, void* stream) {
   bool empty;
-  int st = check_grouped(x_perm, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up, s_gate,
-                         s_up, h_work, &empty);
+  int st = check_grouped(x, offsets, e_count, max_rows, d, f, w_dtype, w_gate, w_up, s_gate,
+                         s_up, h_work, &empty, row_index, src_rows);
   if (st != MF_OK || empty) return st;
   st = check_grouped(h_work, offsets, e_count, max_rows, d, f, w_dtype, w_down, w_down, s_down,
                      s_down, y_perm, &empty);
   if (st != MF_OK) return st;
   const hipStream_t s = S(stream);
-  enqueue_gate_up(x_perm, offsets, e_count, max_rows, d, f, w_gate, w_up, w_dtype, s_gate, s_up,
-                  h_work, s);
+  enqueue_gate_up(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate, w_up, w_dtype,
+                  s_gate, s_up, h_work, s);
   enqueue_down(h_work, offsets, e_count, max_rows, f, d, w_down, w_dtype, s_down, y_perm, s);
   return finish();
 }
 
 int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w, int64_t T,
-                int32_t k, int32_t d, int64_t max_rows, void* out, int32_t out_dtype,
-                void* stream) {
+                int32_t k, int32_t d, int64_t max_rows, const void* residual, void* out,
+                int32_t out_dtype, void* stream) {
   if (T < 0 || k < 1 || d <= 0 || max_rows < 0) return MF_EINVAL;
   if (out_dtype != MF_BF16 && out_dtype != MF_F32) return MF_EINVAL;
   if (k > 8 || d % 64 != 0 || T > 0xFFFFFFFFLL) return MF_EUNSUPPORTED;
   if (T == 0) return MF_OK;  // zero-size buffers may be NULL
   if (!inv_pos || !topk_w || !out || (!y_perm && max_rows > 0)) return MF_EINVAL;
-  if (!a16(y_perm) || !a16(out)) return MF_EUNSUPPORTED;
-  mf::launch_combine(y_perm, inv_pos, topk_w, T, k, d, max_rows, out, out_dtype == MF_F32,
-                     S(stream));
+  if (!a16(y_perm) || !a16(out) || !a16(residual)) return MF_EUNSUPPORTED;
+  mf::launch_combine(y_perm, inv_pos, topk_w, T, k, d, max_rows, residual, out,
+                     out_dtype == MF_F32, S(stream));
   return finish();
 }
 
@@ -245,7 +249,8 @@ int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s, const 
   const hipStream_t s = S(stream);
   if (dtype == MF_BF16) {
     const int cus = num_cus();
-    mf::launch_gemm_gateup_bf16(x, nullptr, 1, T, d, f_s, w_gate_s, w_up_s, h_work, cus, s);
+    mf::launch_gemm_gateup_bf16(x, nullptr, 0, nullptr, 1, T, d, f_s, w_gate_s, w_up_s, h_work,
+                                cus, s);
     mf::launch_gemm_down_bf16(h_work, nullptr, 1, T, f_s, d, w_down_s, partial, true, cus, s);
   } else {
     mf::launch_dense_f32(static_cast<const float*>(x), static_cast<const float*>(w_gate_s),

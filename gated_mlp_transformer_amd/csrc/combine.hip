@@ -1,7 +1,10 @@
 // Weighted un-permute ("推理计算流梳理", EP 路径: expert outputs summed with the
 // router weights back at the token's source; "「赤兔」Chitu ... MoE":
 // token_unpermutation):
-//   out[t] = sum_{j : inv_pos[t,j] valid} w[t,j] * y_perm[inv_pos[t,j]].
+//   out[t] = sum_{j : inv_pos[t,j] valid} w[t,j] * y_perm[inv_pos[t,j]]  (+ residual[t])
+// The optional residual is the Pre-Norm block's skip connection
+// ("推理计算流梳理", Norm&Residual: the layer output is the residual stream plus
+// the FFN of its normalised copy), added after the weighted sum.
 //
 // A gather, not a scatter: one 256-thread workgroup per token reads at most k
 // rows of y_perm with 16-byte loads and sums them in fp32 in slot order, so the
@@ -16,7 +19,8 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ y,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int k, int d,
-                                                      int64_t max_rows, void* __restrict__ out) {
+                                                      int64_t max_rows, const void* __restrict__ residual,
+                                                      void* __restrict__ out) {
   const int64_t t = blockIdx.x;
   int64_t pos[8];
   float wt[8];
@@ -48,6 +52,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[j], f[e], acc[e]);
       }
     }
+    if (residual != nullptr) {
+      if constexpr (OUT_F32) {
+        const float* rr = static_cast<const float*>(residual) + t * d + static_cast<int64_t>(v) * 8;
+        const u32x4 r0 = ld16(rr), r1 = ld16(rr + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += __uint_as_float(r0[e]);
+          acc[4 + e] += __uint_as_float(r1[e]);
+        }
+      } else {
+        float rf[8];
+        unpack_bf16x8(ld16(static_cast<const bf16_t*>(residual) + t * d + static_cast<int64_t>(v) * 8),
+                      rf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += rf[e];
+      }
+    }
     if constexpr (OUT_F32) {
       float* o = static_cast<float*>(out) + t * d + static_cast<int64_t>(v) * 8;
       st16(o, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
@@ -62,14 +83,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__
 }
 
 void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w, int64_t T, int k,
-                    int d, int64_t max_rows, void* out, bool out_f32, hipStream_t s) {
+                    int d, int64_t max_rows, const void* residual, void* out, bool out_f32,
+                    hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(T));
   if (out_f32)
     combine_kernel<true><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(y_perm), inv_pos, w, k,
-                                              d, max_rows, out);
+                                              d, max_rows, residual, out);
   else
     combine_kernel<false><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(y_perm), inv_pos, w, k,
-                                               d, max_rows, out);
+                                               d, max_rows, residual, out);
 }
 
 }  // namespace mf

@@ -75,10 +75,25 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, f3
 
 // ---- wave reductions ----------------------------------------------------
 
+// Wave-wide sum, uniform result. DPP lane moves (register speed): two quad
+// permutations and the two mirrors give every lane its 16-lane row's sum;
+// row_bcast15 adds row 0 into row 1 and row 2 into row 3, row_bcast31 adds
+// lane 31 into rows 2 and 3, so lane 63 ends with the sum of all 64 lanes.
+// Rows outside a step's row mask receive 0 (the DPP "old" value). The order
+// of the additions is fixed, so the result is deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF,
+                                                    false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f32<0x140, 0xF>(v);  // row_mirror
+  v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ---- math ----------------------------------------------------------------

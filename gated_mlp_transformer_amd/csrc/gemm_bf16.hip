@@ -64,7 +64,11 @@ constexpr int FRAG = 1024;     // bytes of one packed 32x16 weight fragment
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 struct GemmParams {
-  const char* a;           // [max_rows, K] bf16
+  const char* a;           // [max_rows, K] bf16, or [a_src_rows, K] when a_rows is set
+  const int32_t* a_rows;   // nullptr, or [max_rows]: row r of the GEMM's A is row a_rows[r]
+                           // of `a` (clamped to [0, a_src_rows)): the gather of the
+                           // permutation done inside the A load
+  int a_src_rows;
   const char* b0;          // packed weights (gate, or down): [groups][nb][K/16] fragments
   const char* b1;          // packed weights (up; gated only)
   char* c;                 // [max_rows, ldc] bf16 or f32 (per K split, see c_split)
@@ -272,7 +276,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < MT / 2; ++i) {
       const int r = ld_r + 64 * i;
-      ap[i] = p.a + static_cast<int64_t>(row0 + (r < rows_valid ? r : 0)) * Kb + kofs_a + ld_c * 16;
+      int arow = row0 + (r < rows_valid ? r : 0);
+      if (p.a_rows != nullptr) arow = clampi(p.a_rows[arow], 0, p.a_src_rows - 1);
+      ap[i] = p.a + static_cast<int64_t>(arow) * Kb + kofs_a + ld_c * 16;
     }
     const char* bp[2];
 #pragma unroll
@@ -383,10 +389,12 @@ int persistent_grid(int64_t max_rows, int bm, int e_count, bool dense, int nt, i
 
 }  // namespace
 
-void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
-                             int K, int N, const void* w_gate, const void* w_up, void* h,
-                             int num_cus, hipStream_t s) {
-  GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_gate),
+void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src_rows,
+                             const int32_t* offsets, int e_count, int64_t max_rows, int K, int N,
+                             const void* w_gate, const void* w_up, void* h, int num_cus,
+                             hipStream_t s) {
+  GemmParams p{static_cast<const char*>(a), a_rows, static_cast<int>(a_src_rows),
+               static_cast<const char*>(w_gate),
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
                static_cast<int>(max_rows), K, N / 32, N, N, K, 0};
   const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
@@ -397,7 +405,7 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                            int K, int N, const void* w_down, void* y, bool out_f32, int num_cus,
                            hipStream_t s) {
-  GemmParams p{static_cast<const char*>(a), static_cast<const char*>(w_down), nullptr,
+  GemmParams p{static_cast<const char*>(a), nullptr, 0, static_cast<const char*>(w_down), nullptr,
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
                N, N, K, 0};
   const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
@@ -413,7 +421,7 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
   // One group of `rows` rows against n_valid (<= 256) packed weight rows, K
   // split in `splits` equal ranges; split y writes its fp32 partial product to
   // c_partials[y][rows][n_valid].
-  GemmParams p{static_cast<const char*>(a), static_cast<const char*>(b), nullptr,
+  GemmParams p{static_cast<const char*>(a), nullptr, 0, static_cast<const char*>(b), nullptr,
                reinterpret_cast<char*>(c_partials), nullptr, 1, static_cast<int>(rows), K,
                (n_valid + 31) / 32, n_valid, n_valid, K / splits,
                rows * static_cast<int64_t>(n_valid)};

@@ -43,7 +43,9 @@ constexpr int SLAB = 128; // K depth per scale block
 constexpr int MAX_GROUPS = 256;
 
 struct Fp8Params {
-  const char* a;           // [max_rows, K] bf16
+  const char* a;           // [max_rows, K] bf16, or [a_src_rows, K] when a_rows is set
+  const int32_t* a_rows;   // nullptr, or [max_rows]: row r of A is row a_rows[r] of `a`
+  int a_src_rows;          // (clamped to [0, a_src_rows))
   const uint8_t* b0;       // packed fp8 weights (gate, or down), see pack.hip
   const uint8_t* b1;       // packed fp8 weights (up; gated only)
   const float* s0;         // [groups, N/128, K/128]
@@ -132,7 +134,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
     for (int m0 = beg; m0 < end; m0 += 16) {
       const int rows_valid = min(16, end - m0);
       const bool arow_ok = lr < rows_valid;
-      const char* ap = p.a + static_cast<int64_t>(m0 + (arow_ok ? lr : 0)) * K * 2 + 64 * lg;
+      int arow = m0 + (arow_ok ? lr : 0);
+      if (p.a_rows != nullptr) arow = clampi(p.a_rows[arow], 0, p.a_src_rows - 1);
+      const char* ap = p.a + static_cast<int64_t>(arow) * K * 2 + 64 * lg;
 
       f32x4 acc[R];
 #pragma unroll
@@ -203,11 +207,12 @@ unsigned fp8_grid(int e_count, int N, int ntw, int num_cus) {
 
 }  // namespace
 
-void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
-                            int K, int N, const void* w_gate, const void* w_up,
-                            const float* s_gate, const float* s_up, void* h, int num_cus,
-                            hipStream_t s) {
-  Fp8Params p{static_cast<const char*>(a), static_cast<const uint8_t*>(w_gate),
+void launch_gemm_gateup_fp8(const void* a, const int32_t* a_rows, int64_t a_src_rows,
+                            const int32_t* offsets, int e_count, int64_t max_rows, int K, int N,
+                            const void* w_gate, const void* w_up, const float* s_gate,
+                            const float* s_up, void* h, int num_cus, hipStream_t s) {
+  Fp8Params p{static_cast<const char*>(a), a_rows, static_cast<int>(a_src_rows),
+              static_cast<const uint8_t*>(w_gate),
               static_cast<const uint8_t*>(w_up), s_gate, s_up, static_cast<char*>(h), offsets,
               e_count, static_cast<int>(max_rows), K, N};
   gemm_fp8_kernel<true><<<dim3(fp8_grid(e_count, N, 256, num_cus)), 256, 0, s>>>(p);
@@ -216,7 +221,7 @@ void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count, 
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                           int K, int N, const void* w_down, const float* s_down, void* y,
                           int num_cus, hipStream_t s) {
-  Fp8Params p{static_cast<const char*>(a), static_cast<const uint8_t*>(w_down), nullptr, s_down,
+  Fp8Params p{static_cast<const char*>(a), nullptr, 0, static_cast<const uint8_t*>(w_down), nullptr, s_down,
               nullptr, static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N};
   gemm_fp8_kernel<false><<<dim3(fp8_grid(e_count, N, 512, num_cus)), 256, 0, s>>>(p);
 }

@@ -29,10 +29,12 @@ void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool 
                  hipStream_t s);
 
 // bf16 MFMA grouped GEMMs on packed weights. offsets == nullptr means one group
-// of max_rows rows.
-void launch_gemm_gateup_bf16(const void* a, const int32_t* offsets, int e_count,
-                             int64_t max_rows, int K, int N, const void* w_gate,
-                             const void* w_up, void* h, int num_cus, hipStream_t s);
+// of max_rows rows. a_rows (optional) makes row r of A the row a_rows[r] of a
+// (a_src_rows rows): the permutation's gather fused into the A load.
+void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src_rows,
+                             const int32_t* offsets, int e_count, int64_t max_rows, int K,
+                             int N, const void* w_gate, const void* w_up, void* h, int num_cus,
+                             hipStream_t s);
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count,
                            int64_t max_rows, int K, int N, const void* w_down,
                            void* y, bool out_f32, int num_cus, hipStream_t s);
@@ -43,17 +45,17 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
                                int splits, float* c_partials, int num_cus, hipStream_t s);
 
 // fp8-weight (block-scaled) grouped GEMMs.
-void launch_gemm_gateup_fp8(const void* a, const int32_t* offsets, int e_count,
-                            int64_t max_rows, int K, int N, const void* w_gate,
-                            const void* w_up, const float* s_gate, const float* s_up,
-                            void* h, int num_cus, hipStream_t s);
+void launch_gemm_gateup_fp8(const void* a, const int32_t* a_rows, int64_t a_src_rows,
+                            const int32_t* offsets, int e_count, int64_t max_rows, int K,
+                            int N, const void* w_gate, const void* w_up, const float* s_gate,
+                            const float* s_up, void* h, int num_cus, hipStream_t s);
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
                           int64_t max_rows, int K, int N, const void* w_down,
                           const float* s_down, void* y, int num_cus, hipStream_t s);
 
 void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w,
-                    int64_t T, int k, int d, int64_t max_rows, void* out,
-                    bool out_f32, hipStream_t s);
+                    int64_t T, int k, int d, int64_t max_rows, const void* residual,
+                    void* out, bool out_f32, hipStream_t s);
 
 // fp32 dense shard (FMA, no MFMA).
 void launch_dense_f32(const float* x, const float* w_gate, const float* w_up,

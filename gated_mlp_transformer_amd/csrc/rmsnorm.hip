@@ -30,6 +30,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
       if (vi < nvec) v[i] = ld16(xr + static_cast<size_t>(vi) * 16);
     }
   };
+  // gamma is the same for every row: held in registers for the wave's rows
+  u32x4 g[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int vi = lane + i * kWave;
+    if (vi < nvec) g[i] = ld16(gr + static_cast<size_t>(vi) * 16);
+  }
   u32x4 cur[MAXV], nxt[MAXV];
   if (row < rows) load(cur, row);
   for (; row < rows; row += stride) {
@@ -60,19 +67,18 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
     for (int i = 0; i < MAXV; ++i) {
       const int vi = lane + i * kWave;
       if (vi < nvec) {
-        const u32x4 g = ld16(gr + static_cast<size_t>(vi) * 16);
         u32x4 o;
         if constexpr (sizeof(T) == 2) {
           float f[8], gf[8], res[8];
           unpack_bf16x8(cur[i], f);
-          unpack_bf16x8(g, gf);
+          unpack_bf16x8(g[i], gf);
 #pragma unroll
           for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
           o = pack_bf16x8(res);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            o[e] = __float_as_uint(__uint_as_float(g[e]) * (__uint_as_float(cur[i][e]) * r));
+            o[e] = __float_as_uint(__uint_as_float(g[i][e]) * (__uint_as_float(cur[i][e]) * r));
         }
         st16(yr + static_cast<size_t>(vi) * 16, o);
       }

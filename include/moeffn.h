@@ -174,7 +174,15 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
  * rank runs many experts as one grouped GEMM); "「赤兔」Chitu ... MoE", experts
  * (BatchedExperts; one kernel for all experts; block-fp8 quantised experts).
  *
- * x_perm   [max_rows, d] bf16    rows grouped by expert (moe_permute output)
+ * x        the grouped input, in one of two forms:
+ *          row_index == NULL: x is X_perm [max_rows, d] bf16, rows grouped by
+ *            expert (moe_permute's gathered output);
+ *          row_index != NULL: x is the un-permuted [src_rows, d] bf16 tensor and
+ *            row r of X_perm is x[row_index[r]] (row_index = moe_permute's
+ *            src_token, [max_rows] int32, entries clamped to [0, src_rows)):
+ *            the gather is done inside the GEMM's A load and moe_permute can
+ *            run with x == NULL (indices only).
+ * src_rows rows of x when row_index != NULL (>= 1), else ignored
  * offsets  [e_count+1] int32     device; expert e owns rows [offsets[e], offsets[e+1])
  * w_gate, w_up [e_count, f, d]   w_dtype (MF_BF16, or MF_FP8_E4M3 codes), packed
  * w_down   [e_count, d, f]       w_dtype, packed (pack_weights with groups = e_count)
@@ -190,22 +198,23 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
  * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 256 == 0;
  * fp8: d % 256 == 0 and f % 256 == 0.
  */
-int grouped_swiglu(const void* x_perm, const int32_t* offsets, int32_t e_count,
-                   int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
-                   const void* w_up, const void* w_down, int32_t w_dtype,
-                   const float* s_gate, const float* s_up, const float* s_down,
-                   void* h_work, void* y_perm, void* stream);
+int grouped_swiglu(const void* x, const int32_t* row_index, int64_t src_rows,
+                   const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
+                   int32_t f, const void* w_gate, const void* w_up, const void* w_down,
+                   int32_t w_dtype, const float* s_gate, const float* s_up,
+                   const float* s_down, void* h_work, void* y_perm, void* stream);
 
 /*
  * grouped_gate_up - the first half of grouped_swiglu on its own:
  *   H[o_e:o_{e+1}] = SiLU(X_perm W_gate_e) * (X_perm W_up_e)
- * Same passages, arguments, layouts and requirements as grouped_swiglu
- * (h_out is its h_work). The SiLU product is fused into the GEMM epilogue.
+ * Same passages, arguments (x, row_index, src_rows included), layouts and
+ * requirements as grouped_swiglu (h_out is its h_work). The SiLU product is
+ * fused into the GEMM epilogue.
  */
-int grouped_gate_up(const void* x_perm, const int32_t* offsets, int32_t e_count,
-                    int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
-                    const void* w_up, int32_t w_dtype, const float* s_gate,
-                    const float* s_up, void* h_out, void* stream);
+int grouped_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
+                    const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
+                    int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+                    const float* s_gate, const float* s_up, void* h_out, void* stream);
 
 /*
  * grouped_down - the second half of grouped_swiglu on its own:
@@ -218,7 +227,11 @@ int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
                  int32_t w_dtype, const float* s_down, void* y_perm, void* stream);
 
 /*
- * moe_combine - out[t] = sum_{j : inv_pos[t,j] >= 0} topk_w[t,j] * y_perm[inv_pos[t,j]].
+ * moe_combine - out[t] = sum_{j : inv_pos[t,j] >= 0} topk_w[t,j] * y_perm[inv_pos[t,j]]
+ *                        (+ residual[t]).
+ * The optional residual is the Pre-Norm block's skip connection ("推理计算流梳理",
+ * Norm&Residual: the layer output is the residual stream plus the FFN of its
+ * normalised copy); with expert parallelism it is passed on one rank only.
  *
  * "推理计算流梳理", EP 路径: the expert outputs are summed with the router
  * weights back at the token's source ("「赤兔」Chitu ... MoE":
@@ -227,12 +240,14 @@ int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
  * and the outputs of disjoint expert ranges add up to the full FFN output.
  *
  * y_perm  [max_rows, d] bf16; inv_pos [T, k] int32 (entries < 0 or >= max_rows
- * are skipped); topk_w [T, k] f32; out [T, d] out_dtype (MF_BF16 or MF_F32).
- * fp32 accumulation in slot order j = 0..k-1. Requires 1 <= k <= 8, d % 64 == 0.
+ * are skipped); topk_w [T, k] f32; residual [T, d] out_dtype or NULL; out
+ * [T, d] out_dtype (MF_BF16 or MF_F32; may alias residual).
+ * fp32 accumulation in slot order j = 0..k-1, then the residual is added.
+ * Requires 1 <= k <= 8, d % 64 == 0.
  */
 int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
-                int64_t T, int32_t k, int32_t d, int64_t max_rows, void* out,
-                int32_t out_dtype, void* stream);
+                int64_t T, int32_t k, int32_t d, int64_t max_rows, const void* residual,
+                void* out, int32_t out_dtype, void* stream);
 
 /*
  * tp_shard_mlp - one tensor-parallel shard of the dense gated MLP:

@@ -318,14 +318,18 @@ def experts(x_perm, offsets, weights) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
-def combine(y_perm, inv_pos, w) -> np.ndarray:
-    """``out[t] = Σ_{j : inv_pos[t,j] >= 0} w[t,j] · y_perm[inv_pos[t,j]]``.
+def combine(y_perm, inv_pos, w, residual=None) -> np.ndarray:
+    """``out[t] = Σ_{j : inv_pos[t,j] >= 0} w[t,j] · y_perm[inv_pos[t,j]]`` (+ ``residual[t]``).
 
     [P1] EP 路径: the expert outputs are summed with the router weights back
     at the token's source. READING R18: the global weights are used unchanged
     (no renormalisation over the local experts), so a token with no local
     expert gets 0 and the outputs of disjoint expert ranges add up to the
     all-local result. The sum runs over slots in order j = 0..k-1.
+
+    ``residual`` (optional, [T, d]): [P1] Norm&Residual, the Pre-Norm block's
+    output is the residual stream R plus the FFN of its normalised copy; the
+    skip connection is added once, after the expert sum.
     """
     y_perm = np.asarray(y_perm, dtype=np.float64)
     inv_pos = np.asarray(inv_pos)
@@ -337,6 +341,8 @@ def combine(y_perm, inv_pos, w) -> np.ndarray:
         m = inv_pos[:, j] >= 0
         if m.any():
             out[m] += w[m, j][:, None] * y_perm[inv_pos[m, j]]
+    if residual is not None:
+        out = out + np.asarray(residual, dtype=np.float64)
     return out
 
 

@@ -118,9 +118,11 @@ def test_permute_validation(lib):
 
 
 def test_grouped_swiglu_validation(lib):
-    def call(ec=4, rows=64, d=256, f=256, wdt=BF16, s=(N, N, N), x=P):
-        return lib.grouped_swiglu(x, P, ec, rows, d, f, P, P, P, wdt, *s, P, P, N)
+    def call(ec=4, rows=64, d=256, f=256, wdt=BF16, s=(N, N, N), x=P, ri=N, src=0):
+        return lib.grouped_swiglu(x, ri, src, P, ec, rows, d, f, P, P, P, wdt, *s, P, P, N)
     assert call(x=N) == MF_EINVAL
+    assert call(ri=P, src=0) == MF_EINVAL                  # gathered input needs its row count
+    assert call(ri=P, src=-3) == MF_EINVAL
     assert call(ec=0) == MF_EINVAL
     assert call(wdt=F32) == MF_EINVAL
     assert call(wdt=FP8) == MF_EINVAL                      # fp8 needs scales
@@ -133,11 +135,13 @@ def test_grouped_swiglu_validation(lib):
 
 
 def test_combine_and_shard_validation(lib):
-    assert lib.moe_combine(P, P, N, 4, 8, 64, 32, P, BF16, N) == MF_EINVAL
-    assert lib.moe_combine(P, P, P, 4, 9, 64, 32, P, BF16, N) == MF_EUNSUPPORTED
-    assert lib.moe_combine(P, P, P, 4, 8, 72, 32, P, BF16, N) == MF_EUNSUPPORTED
-    assert lib.moe_combine(P, P, P, 4, 8, 64, 32, P, FP8, N) == MF_EINVAL
-    assert lib.moe_combine(P, P, P, 0, 8, 64, 32, P, BF16, N) == MF_OK
+    assert lib.moe_combine(P, P, N, 4, 8, 64, 32, N, P, BF16, N) == MF_EINVAL
+    assert lib.moe_combine(P, P, P, 4, 9, 64, 32, N, P, BF16, N) == MF_EUNSUPPORTED
+    assert lib.moe_combine(P, P, P, 4, 8, 72, 32, N, P, BF16, N) == MF_EUNSUPPORTED
+    assert lib.moe_combine(P, P, P, 4, 8, 64, 32, N, P, FP8, N) == MF_EINVAL
+    assert lib.moe_combine(P, P, P, 4, 8, 64, 32, ctypes.c_void_p(0x100008), P, BF16, N) \
+        == MF_EUNSUPPORTED                                 # misaligned residual
+    assert lib.moe_combine(P, P, P, 0, 8, 64, 32, N, P, BF16, N) == MF_OK
     assert lib.tp_shard_mlp(P, P, P, N, 4, 256, 256, BF16, P, P, N) == MF_EINVAL
     assert lib.tp_shard_mlp(P, P, P, P, 4, 192, 256, BF16, P, P, N) == MF_EUNSUPPORTED
     assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 128, BF16, P, P, N) == MF_EUNSUPPORTED

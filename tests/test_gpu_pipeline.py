@@ -10,8 +10,9 @@ raw inputs:
     except for tokens whose 8th/9th biased-score gap is below 1e-6 (then any
     valid top-8 within that band is accepted); weights within tolerance.
   * permutation, on the GPU's ids: counts, offsets, src_token, inv_pos
-    bit-exact; x_perm equal to V[src_token] bit for bit.
-  * expert GEMMs, on the GPU's x_perm and H: tolerance on H and Y_perm.
+    bit-exact (the layer permutes indices only).
+  * expert GEMMs, on the rows V[src_token] that the gate/up GEMM gathers in
+    its A load, and on the GPU's H: tolerance on H and Y_perm.
   * combine, on the GPU's Y_perm: tolerance.
   * end to end: the oracle's fp64 sub-block from the raw x with the routed
     sets the GPU chose (accepted above): tolerance on the output.
@@ -99,10 +100,10 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
     assert np.array_equal(to_i64(layer.offsets), offsets)
     assert np.array_equal(to_i64(layer.src_token)[:S], src)
     assert np.array_equal(to_i64(layer.inv_pos), inv)
-    assert torch.equal(layer.x_perm[:S].cpu(), layer.v.cpu()[torch.from_numpy(src)])
 
-    # expert GEMMs on the GPU's x_perm (H) and H (Y_perm): all rows, sampled columns
-    xp = to_f64(layer.x_perm[:S])
+    # expert GEMMs on the gathered rows V[src_token] (H) and the GPU's H
+    # (Y_perm): all rows, sampled columns
+    xp = v_gpu[src]
     h_gpu = to_f64(layer.h[:S])
     y_gpu = to_f64(layer.y_perm[:S])
     hc = np.arange(f) if col_sample is None else np.asarray(col_sample)

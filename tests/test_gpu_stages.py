@@ -209,18 +209,32 @@ def _oracle_weights(W, e, wdtype):
     ("fp8", [1, 3, 0, 17, 2, 16], 256, 512),
     ("fp8", [40], 512, 256),
 ])
-def test_grouped_swiglu(g, wdtype, counts, d, f):
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_swiglu(g, wdtype, counts, d, f, gather):
     ec = len(counts)
     S = int(sum(counts))
     max_rows = S + 5
     W = _expert_weights(ec, d, f, wdtype, seed=S + d)
-    x_perm = synth.normal((max_rows, d), name="t.gs.x", sub=S, device=DEV)
     offsets = _offsets(counts)
     h = torch.full((max_rows, f), float("nan"), dtype=torch.bfloat16, device=DEV)
     y = torch.full((max_rows, d), float("nan"), dtype=torch.bfloat16, device=DEV)
     pw = [g.pack_weights(W[k_]) for k_ in ("w_gate", "w_up", "w_down")]
-    g.grouped_swiglu(x_perm, offsets, *pw, W.get("s_gate"),
-                     W.get("s_up"), W.get("s_down"), h_work=h, y_perm=y)
+    if gather:
+        # the GEMM gathers row r from x_src[row_index[r]]; out-of-range indices
+        # are clamped into the source rows
+        src_rows = max(1, S // 3 + 7)
+        x_src = synth.normal((src_rows, d), name="t.gs.xsrc", sub=S, device=DEV)
+        ri = synth.integers((max_rows,), 0, src_rows, name="t.gs.ri", sub=S).to(torch.int32)
+        if S >= 2:
+            ri[0], ri[S - 1] = -5, src_rows + 11
+        ri = ri.to(DEV)
+        x_perm = x_src[ri.long().clamp(0, src_rows - 1)].contiguous()
+        g.grouped_swiglu(x_src, offsets, *pw, W.get("s_gate"), W.get("s_up"), W.get("s_down"),
+                         row_index=ri, h_work=h, y_perm=y)
+    else:
+        x_perm = synth.normal((max_rows, d), name="t.gs.x", sub=S, device=DEV)
+        g.grouped_swiglu(x_perm, offsets, *pw, W.get("s_gate"),
+                         W.get("s_up"), W.get("s_down"), h_work=h, y_perm=y)
     torch.cuda.synchronize()
     # rows past the last expert are never written
     assert torch.isnan(h[S:].float()).all() and torch.isnan(y[S:].float()).all()
@@ -247,8 +261,11 @@ def test_grouped_swiglu(g, wdtype, counts, d, f):
 
 # ------------------------------------------------------------------ combine --
 
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_combine(g, out_dtype):
+@pytest.mark.parametrize("out_dtype,with_residual", [(torch.bfloat16, False),
+                                                     (torch.float32, False),
+                                                     (torch.bfloat16, True),
+                                                     (torch.float32, True)])
+def test_combine(g, out_dtype, with_residual):
     T, E, k, d = 300, 64, 8, 256
     idx = routing_ids(T, E, k, seed=11)
     res = g.moe_permute(idx, 8, 24, None)
@@ -256,13 +273,16 @@ def test_combine(g, out_dtype):
     y_perm = synth.normal((S_max, d), name="t.comb.y", device=DEV)
     w = torch.rand((T, k), generator=torch.Generator(DEV).manual_seed(3), device=DEV) + 0.05
     w = (w / w.sum(1, keepdim=True)).float().contiguous()
-    out = g.moe_combine(y_perm, res.inv_pos, w, out_dtype=out_dtype)
+    r = synth.normal((T, d), name="t.comb.r", dtype=out_dtype, device=DEV) if with_residual else None
+    out = g.moe_combine(y_perm, res.inv_pos, w, out_dtype=out_dtype, residual=r)
     torch.cuda.synchronize()
-    ref = oracle.combine(to_f64(y_perm), to_i64(res.inv_pos), to_f64(w))
+    ref = oracle.combine(to_f64(y_perm), to_i64(res.inv_pos), to_f64(w),
+                         residual=None if r is None else to_f64(r))
     none_local = np.all(to_i64(res.inv_pos) < 0, axis=1)
     assert none_local.any() and (~none_local).any()
     got = to_f64(out)
-    assert np.all(got[none_local] == 0)
+    # no local expert: the output is the residual (or 0) exactly
+    assert np.all(got[none_local] == (0 if r is None else to_f64(r)[none_local]))
     tol = dict(rel=5e-3, max_abs=2e-2) if out_dtype == torch.bfloat16 else dict(rel=1e-6, max_abs=1e-5)
     assert_fp("combine", got, ref, **tol)
 

@@ -322,6 +322,24 @@ def test_combine_identity_expert_returns_input():
     assert np.allclose(out, x, rtol=1e-14, atol=1e-14)
 
 
+def test_combine_residual_passes_through_without_local_experts():
+    # [P1] Norm&Residual: block output = R + FFN(V). A token none of whose
+    # experts is local has FFN part 0 on this rank, so its output is exactly R;
+    # elsewhere the residual is the difference between the two combines.
+    T, E, k, d = 40, 16, 8, 5
+    idx = _routing(T, E, k, 45)
+    r = rng(46)
+    x, R = r.standard_normal((T, d)), r.standard_normal((T, d))
+    w = r.random((T, k)) + 0.1
+    w /= w.sum(1, keepdims=True)
+    _, _, _, inv, xp = oracle.permute(idx, 0, 2, x)
+    none = np.all(inv < 0, axis=1)
+    assert none.any() and (~none).any()
+    with_r = oracle.combine(xp, inv, w, residual=R)
+    assert np.array_equal(with_r[none], R[none])
+    assert np.allclose(with_r - oracle.combine(xp, inv, w), R, rtol=0, atol=1e-12)
+
+
 def test_expert_parallel_partials_sum_to_all_local_output():
     # Disjoint expert ranges (8 ranks of 2 experts) give partial outputs that
     # add up to the all-local output: the combine keeps the global weights.
