@@ -78,6 +78,29 @@ def moe_work(T, d, f, E, k, S, active, ec, welt):
     }
 
 
+def measured_traffic(kernel: str, profile: str):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, calibrated) as
+    recorded in profiles/<profile>, or None when the kernel's source has changed
+    since the counters were taken (the record carries the source's sha256)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    pat = re.compile(r"bench-traffic: kernel=(\S+) source=(\S+) sha256=([0-9a-f]+) bytes_per_launch=(\d+)")
+    for line in open(path, encoding="utf-8"):
+        m = pat.search(line)
+        if m and m.group(1) == kernel:
+            src = os.path.join(ROOT, m.group(2))
+            if not os.path.exists(src):
+                return None
+            with open(src, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != m.group(3):
+                    return None
+            return int(m.group(4))
+    return None
+
+
 def stage_report(work, us):
     out = {}
     for name, w in work.items():
@@ -347,7 +370,12 @@ def main():
         "roofline": {"kernel": "grouped_gate_up (bf16 MFMA grouped GEMM + SiLU*up epilogue)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     # HBM bytes per launch from the committed rocprofv3 counters
+                     # (null once the kernel source differs from the profiled one)
+                     "traffic": measured_traffic("grouped_gate_up",
+                                                 "moe_prefill_8192tok_hbm_counters.md"),
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": int(w_dom["bytes"]),
                      "hbm_gb_s": round(w_dom["bytes"] / t_dom / 1e9, 1)},
         "stages": stages,
         "grouped_gemm_mfma_frac": round(
