@@ -85,9 +85,14 @@ struct GemmParams {
 };
 
 // A stage row is 64 bytes (four 16-byte chunks); chunk c of row r sits at
-// chunk c ^ ((r/2) % 4), so eight consecutive rows of one chunk (a fragment
-// read) and two rows of four chunks (a row write) both hit distinct banks.
-__device__ __forceinline__ int swz(int r, int chunk) { return r * ROWB + ((chunk ^ ((r >> 1) & 3)) << 4); }
+// chunk c ^ f(r) with f(r) = ((r >> 1) ^ (r >> 3)) % 4. A 32-row fragment read
+// (one logical chunk of consecutive rows) then hits distinct banks in every
+// group of 16 lanes of a 64-bank LDS (rows r and r + 8 no longer collide), and
+// in every group of 8 lanes of a 32-bank one; a row write (four chunks of a
+// row) is a permutation of the row's chunks, conflict-free either way.
+__device__ __forceinline__ int swz(int r, int chunk) {
+  return r * ROWB + ((chunk ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
