@@ -88,8 +88,101 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
   }
 }
 
+// Rows that fill a whole number of 16-byte vectors per lane (d a multiple of
+// 64 * 16 / sizeof(T)): no per-lane predicates (they compile to branches
+// around every load and store), no register prefetch of the next row, so the
+// kernel stays small and many waves per SIMD keep the loads in flight; one
+// row per wave at a time, gamma re-read from cache per row.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
+                                                           T* y, int64_t rows, int d, float eps) {
+  const int lane = threadIdx.x % kWave;
+  const char* gr = reinterpret_cast<const char*>(gamma) + lane * 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; row < rows;
+       row += stride) {
+    const char* xr = reinterpret_cast<const char*>(x + row * d) + lane * 16;
+    u32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = ld16(xr + i * kWave * 16);
+    // sum of squares; the pairs are unpacked here by two ALU instructions the
+    // compiler cannot merge with the output pass's unpacking, so that no
+    // unpacked copy of the row stays in registers between the passes
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float lo, hi;
+          asm("v_lshlrev_b32 %0, 16, %2\n\tv_and_b32 %1, 0xffff0000, %2"
+              : "=&v"(lo), "=&v"(hi)
+              : "v"(v[i][e]));
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = __uint_as_float(v[i][e]);
+          ss = fmaf(f, f, ss);
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+    char* yr = reinterpret_cast<char*>(y + row * d) + lane * 16;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const u32x4 g = ld16(gr + i * kWave * 16);
+      u32x4 o;
+      if constexpr (sizeof(T) == 2) {
+        float f[8], gf[8], res[8];
+        unpack_bf16x8(v[i], f);
+        unpack_bf16x8(g, gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
+        o = pack_bf16x8(res);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = __float_as_uint(__uint_as_float(g[e]) * (__uint_as_float(v[i][e]) * r));
+      }
+      st16(yr + i * kWave * 16, o);
+    }
+  }
+}
+
+namespace {
+
+template <typename T>
+bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d, float eps,
+                 hipStream_t s) {
+  const int per_lane = d * static_cast<int>(sizeof(T)) / (16 * kWave);  // vectors per lane
+  if (d * static_cast<int>(sizeof(T)) % (16 * kWave) != 0) return false;
+  int64_t blocks = (rows + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
+  auto* xp = static_cast<const T*>(x);
+  auto* gp = static_cast<const T*>(gamma);
+  auto* yp = static_cast<T*>(y);
+  switch (per_lane) {
+    case 1: rmsnorm_full_kernel<T, 1><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 2: rmsnorm_full_kernel<T, 2><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 4: rmsnorm_full_kernel<T, 4><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 8: rmsnorm_full_kernel<T, 8><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 16: rmsnorm_full_kernel<T, 16><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    default: return false;
+  }
+}
+
+}  // namespace
+
 void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
                     float eps, bool bf16, hipStream_t s) {
+  if (bf16 ? launch_full<bf16_t>(x, gamma, y, T, d, eps, s)
+           : launch_full<float>(x, gamma, y, T, d, eps, s))
+    return;
   // about two rows per wave: enough waves to fill the chip, each with a row in flight
   int64_t blocks = (T + 7) / 8;
   if (blocks > 2048) blocks = 2048;

@@ -76,8 +76,9 @@ size_t route_workspace_bytes(int64_t T, int d, int E) {
   return static_cast<size_t>(route_splits(T, d)) * static_cast<size_t>(T) * E * sizeof(float);
 }
 
+template <int SPLITS>
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ zp,
-                                                           int splits, const float* __restrict__ bias,
+                                                           const float* __restrict__ bias,
                                                            int64_t T, int E,
                                                            int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out) {
@@ -87,14 +88,16 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   if (t >= T) return;
   const int64_t split_stride = T * E;
   // All partial logits are loaded before any is added (independent loads in
-  // flight together), then summed in split order.
-  float part[kMaxSplits][4];
+  // flight together), then summed in split order. The loads are
+  // unconditional (experts past E re-read expert E-1 and are masked below):
+  // a load under a per-lane condition would become a branch with its own wait.
+  float part[SPLITS][4];
 #pragma unroll
-  for (int y = 0; y < kMaxSplits; ++y)
+  for (int y = 0; y < SPLITS; ++y)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int e = lane + 64 * c;
-      part[y][c] = (y < splits && e < E) ? zp[y * split_stride + t * E + e] : 0.f;
+      const int e = min(lane + 64 * c, E - 1);
+      part[y][c] = zp[y * split_stride + t * E + e];
     }
   // candidates of this lane: experts lane + 64c; key order in the high word,
   // 255 - id in the low word (E <= 256), invalid experts at the bottom
@@ -105,9 +108,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     const int e = lane + 64 * c;
     float z = 0.f;
 #pragma unroll
-    for (int y = 0; y < kMaxSplits; ++y) z += part[y][c];
+    for (int y = 0; y < SPLITS; ++y) z += part[y][c];
     s[c] = sigmoidf_(z);
-    kh[c] = e < E ? order_key(s[c] + bias[e]) : 0u;
+    kh[c] = e < E ? order_key(s[c] + bias[min(e, E - 1)]) : 0u;
     kl[c] = static_cast<uint32_t>(255 - e);
   }
   int sel[8];
@@ -172,8 +175,14 @@ void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, 
   const int splits = route_splits(T, d);
   float* zp = static_cast<float*>(workspace);
   launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
-  route_select_kernel<<<dim3(static_cast<unsigned>((T + 3) / 4)), 256, 0, s>>>(zp, splits, bias,
-                                                                               T, E, idx, w);
+  const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+  switch (splits) {  // route_splits returns a power of two <= kMaxSplits
+    case 1: route_select_kernel<1><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 2: route_select_kernel<2><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 4: route_select_kernel<4><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 8: route_select_kernel<8><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+    default: route_select_kernel<kMaxSplits><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+  }
 }
 
 }  // namespace mf
