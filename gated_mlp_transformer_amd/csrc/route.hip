@@ -12,10 +12,13 @@
 //     order: deterministic), applies the sigmoid and the bias, and picks the
 //     top 8 by eight rounds of a wave-wide arg-max on (key descending, id
 //     ascending); the ids are emitted ascending with w = s / sum(s).
-//     The arg-max runs on one 64-bit value per lane, the key mapped to an
-//     order-preserving unsigned integer in the high word and 255 - id in the
-//     low word, reduced across the wave with DPP lane moves (register speed,
-//     no LDS round trips) and read back from the last lane.
+//     A round takes the wave-wide maximum of the keys (mapped to
+//     order-preserving unsigned integers) with DPP max steps at register
+//     speed, then the lowest expert id
+//     that holds it from the wave's ballots of key == max: a lane holds
+//     experts lane + 64c, so the first slot c with a match and its lowest
+//     lane give the id. Only that candidate is retired, so equal keys are
+//     taken in ascending id order over the rounds.
 #include "common.h"
 #include "launch.h"
 
@@ -34,33 +37,26 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One step of a wave-wide max of the pair (hi, lo), compared as hi:lo: every
-// lane takes the larger of its pair and the pair DPP moves to it. Lanes in
-// rows outside ROW_MASK receive their own pair (the DPP "old" value).
+// v from the lane CTRL names; lanes in rows outside ROW_MASK receive 0, the
+// identity of an unsigned max (so the move folds into the max instruction)
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t ph = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROW_MASK, 0xF, false));
-  const uint32_t pl = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROW_MASK, 0xF, false));
-  const bool take = ph > hi || (ph == hi && pl > lo);
-  hi = take ? ph : hi;
-  lo = take ? pl : lo;
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Wave-wide max of (hi, lo); the result is uniform. After the two quad
-// permutations and the two mirrors every lane holds its 16-lane row's max;
-// row_bcast15 folds row 0 into row 1 and row 2 into row 3, row_bcast31 folds
-// lane 31 into row 3, so lane 63 holds the maximum of all 64 lanes.
-__device__ __forceinline__ void wave_max64(uint32_t& hi, uint32_t& lo) {
-  max_step<0xB1, 0xF>(hi, lo);   // quad_perm [1,0,3,2]
-  max_step<0x4E, 0xF>(hi, lo);   // quad_perm [2,3,0,1]
-  max_step<0x141, 0xF>(hi, lo);  // row_half_mirror
-  max_step<0x140, 0xF>(hi, lo);  // row_mirror
-  max_step<0x142, 0xA>(hi, lo);  // row_bcast15 into rows 1 and 3
-  max_step<0x143, 0xC>(hi, lo);  // row_bcast31 into rows 2 and 3
-  hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
-  lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
+// Wave-wide maximum, uniform. After the two quad permutations and the two
+// mirrors every lane holds its 16-lane row's maximum; row_bcast15 folds row 0
+// into row 1 and row 2 into row 3, row_bcast31 folds lane 31 into row 3, so
+// lane 63 holds the maximum of all 64 lanes.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_or0<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_or0<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_or0<0x141, 0xF>(v));  // row_half_mirror
+  v = max(v, dpp_or0<0x140, 0xF>(v));  // row_mirror
+  v = max(v, dpp_or0<0x142, 0xA>(v));  // row_bcast15 into rows 1 and 3
+  v = max(v, dpp_or0<0x143, 0xC>(v));  // row_bcast31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 }  // namespace
@@ -99,44 +95,37 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
       const int e = min(lane + 64 * c, E - 1);
       part[y][c] = zp[y * split_stride + t * E + e];
     }
-  // candidates of this lane: experts lane + 64c; key order in the high word,
-  // 255 - id in the low word (E <= 256), invalid experts at the bottom
-  float s[4];
-  uint32_t kh[4], kl[4];
+  // candidates of this lane: experts lane + 64c, the key s + b mapped to an
+  // order-preserving unsigned integer; experts past E and retired winners
+  // hold 0, below every valid key
+  float sc[4];
+  uint32_t key[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
     float z = 0.f;
 #pragma unroll
     for (int y = 0; y < SPLITS; ++y) z += part[y][c];
-    s[c] = sigmoidf_(z);
-    kh[c] = e < E ? order_key(s[c] + bias[min(e, E - 1)]) : 0u;
-    kl[c] = static_cast<uint32_t>(255 - e);
+    sc[c] = sigmoidf_(z);
+    key[c] = e < E ? order_key(sc[c] + bias[min(e, E - 1)]) : 0u;
   }
   int sel[8];
   float ssel[8];
 #pragma unroll
   for (int round = 0; round < 8; ++round) {
-    uint32_t bh = kh[0], bl = kl[0];
+    const uint32_t m = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
+    uint64_t hit[4];
 #pragma unroll
-    for (int c = 1; c < 4; ++c) {
-      if (kh[c] > bh || (kh[c] == bh && kl[c] > bl)) {
-        bh = kh[c];
-        bl = kl[c];
-      }
-    }
-    wave_max64(bh, bl);
-    const int id = 255 - static_cast<int>(bl);  // uniform
-    const int cw = id >> 6, lw = id & 63;
-    const float sv = cw == 0 ? s[0] : cw == 1 ? s[1] : cw == 2 ? s[2] : s[3];
-    sel[round] = id;
+    for (int c = 0; c < 4; ++c) hit[c] = __builtin_amdgcn_ballot_w64(key[c] == m);
+    const int cw = hit[0] ? 0 : hit[1] ? 1 : hit[2] ? 2 : 3;  // uniform
+    const uint64_t hw = cw == 0 ? hit[0] : cw == 1 ? hit[1] : cw == 2 ? hit[2] : hit[3];
+    const int lw = __builtin_ctzll(hw);
+    const float sv = cw == 0 ? sc[0] : cw == 1 ? sc[1] : cw == 2 ? sc[2] : sc[3];
+    sel[round] = 64 * cw + lw;
     ssel[round] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), lw));
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (c == cw && lane == lw) {  // the owner lane retires the winner
-        kh[c] = 0u;
-        kl[c] = 0u;
-      }
+      if (c == cw && lane == lw) key[c] = 0u;  // the owner lane retires the winner
   }
   // ids ascending (I is a set), scores carried along
 #pragma unroll
