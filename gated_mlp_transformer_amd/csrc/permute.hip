@@ -4,15 +4,20 @@
 //
 // Deterministic without ordered atomics. Tokens are cut into blocks of 256
 // (one 256-thread workgroup, four waves of 64 tokens):
-//   1. mask:    each wave builds, per local expert, the 64-bit mask of its
-//               tokens routed there (LDS atomicOr: an OR is order-free), and
-//               the workgroup writes the masks and the block's count per expert.
-//   2. scan:    one workgroup turns the counts into per-(block, expert) bases,
-//               the per-expert totals and the exclusive offsets.
-//   3. scatter: a slot's row is offsets[e] + base[block][e] + the popcounts of
-//               the earlier waves' masks + the popcount of its own wave's mask
-//               below its lane, i.e. the number of earlier tokens routed to e.
-//   4. gather:  x_perm[r] = x[src_token[r]], 16-byte copies.
+//   1. count:   each workgroup counts its block's slots per local expert (LDS
+//               integer atomics: order-free) and writes the counts.
+//   2. place:   each workgroup takes, per expert, the sum of the earlier
+//               blocks' counts and the total over all blocks (reading the
+//               B x e_count counts itself while that table is small, else
+//               from a one-workgroup scan pass), the exclusive offsets from
+//               an LDS scan of the totals, and per wave and expert the 64-bit
+//               mask of its tokens routed there (LDS atomicOr). A slot's row
+//               is offsets[e] + (earlier blocks' count) + the popcounts of
+//               the earlier waves' masks + the popcount of its own wave's
+//               mask below its lane, i.e. the number of earlier tokens routed
+//               to e.
+//   3. gather:  x_perm[r] = x[src_token[r]], 16-byte copies (only when x is
+//               given).
 #include "common.h"
 #include "launch.h"
 
@@ -23,11 +28,13 @@ namespace {
 constexpr int kBlockTok = 256;
 constexpr int kWaves = 4;
 constexpr int kMaxLocal = 256;
+// largest count table (blocks x local experts) each workgroup of the place
+// pass scans itself; beyond it one workgroup scans it once
+constexpr int64_t kSelfScanMax = 16384;
 
 struct Workspace {
-  int32_t* cnt;       // [B][e_count]
-  int32_t* base;      // [B][e_count]
-  uint64_t* masks;    // [B][4][e_count]
+  int32_t* cnt;       // [B][e_count] slots per block and expert
+  int32_t* base;      // [B][e_count] earlier blocks' slots (scan pass only)
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -38,47 +45,47 @@ Workspace carve(void* ws, int64_t B, int e_count) {
   w.cnt = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * B * e_count);
   w.base = reinterpret_cast<int32_t*>(p);
-  p += align256(sizeof(int32_t) * B * e_count);
-  w.masks = reinterpret_cast<uint64_t*>(p);
   return w;
+}
+
+// inclusive sum over the 256 entries of v (LDS, all 256 threads take part)
+__device__ __forceinline__ void block_inclusive_scan(int* v) {
+  const int e = threadIdx.x;
+  for (int off = 1; off < 256; off <<= 1) {
+    const int x = e >= off ? v[e - off] : 0;
+    __syncthreads();
+    v[e] += x;
+    __syncthreads();
+  }
 }
 
 }  // namespace
 
 size_t permute_workspace_bytes(int64_t T, int e_count) {
   const int64_t B = (T + kBlockTok - 1) / kBlockTok;
-  return 2 * align256(sizeof(int32_t) * B * e_count) +
-         align256(sizeof(uint64_t) * B * kWaves * e_count) + 256;
+  return 2 * align256(sizeof(int32_t) * B * e_count) + 256;
 }
 
-__global__ __launch_bounds__(256) void permute_mask_kernel(const int32_t* __restrict__ idx,
-                                                           int64_t T, int k, int e_begin,
-                                                           int e_count, Workspace ws) {
-  __shared__ unsigned long long m[kWaves][kMaxLocal];
+__global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx,
+                                                            int64_t T, int k, int e_begin,
+                                                            int e_count, Workspace ws) {
+  __shared__ int c[kMaxLocal];
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  for (int i = tid; i < kWaves * kMaxLocal; i += 256) (&m[0][0])[i] = 0ull;
+  c[tid] = 0;
   __syncthreads();
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockTok + tid;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j] - e_begin;
-      if (e >= 0 && e < e_count) atomicOr(&m[wave][e], 1ull << lane);
+      if (e >= 0 && e < e_count) atomicAdd(&c[e], 1);
     }
   }
   __syncthreads();
-  const int64_t b = blockIdx.x;
-  for (int e = tid; e < e_count; e += 256) {
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      c += __popcll(m[w][e]);
-      ws.masks[(b * kWaves + w) * e_count + e] = m[w][e];
-    }
-    ws.cnt[b * e_count + e] = c;
-  }
+  if (tid < e_count) ws.cnt[blockIdx.x * static_cast<int64_t>(e_count) + tid] = c[tid];
 }
 
+// One workgroup: per-(block, expert) bases, per-expert totals and the offsets
+// (for count tables too large for every workgroup of the place pass to scan).
 __global__ __launch_bounds__(256) void permute_scan_kernel(int64_t B, int e_count, Workspace ws,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets) {
@@ -106,34 +113,80 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int64_t B, int e_coun
   }
   sc[e] = e < e_count ? running : 0;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 256 entries
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = e >= off ? sc[e - off] : 0;
-    __syncthreads();
-    sc[e] += v;
-    __syncthreads();
-  }
+  block_inclusive_scan(sc);
   if (e < e_count) offsets[e + 1] = sc[e];
   if (e == 0) offsets[0] = 0;
 }
 
-__global__ __launch_bounds__(256) void permute_scatter_kernel(
-    const int32_t* __restrict__ idx, int64_t T, int k, int e_begin, int e_count, Workspace ws,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ src_token,
-    int32_t* __restrict__ inv_pos) {
+template <bool SELF_SCAN>
+__global__ __launch_bounds__(256) void permute_place_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int k, int e_begin, int e_count, int64_t B,
+    Workspace ws, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ src_token, int32_t* __restrict__ inv_pos) {
+  __shared__ unsigned long long m[kWaves][kMaxLocal];
+  __shared__ int row0[kMaxLocal];  // first row of this block's slots, per expert
+  __shared__ int sc[256];
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int64_t b = blockIdx.x;
+  for (int i = tid; i < kWaves * kMaxLocal; i += 256) (&m[0][0])[i] = 0ull;
+  if constexpr (SELF_SCAN) {
+    // per expert (thread e): earlier blocks' slots and the total
+    int before = 0, total = 0;
+    if (tid < e_count) {
+      int64_t q = 0;
+      for (; q + 8 <= B; q += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = ws.cnt[(q + u) * e_count + tid];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          before += q + u < b ? c[u] : 0;
+          total += c[u];
+        }
+      }
+      for (; q < B; ++q) {
+        const int c = ws.cnt[q * e_count + tid];
+        before += q < b ? c : 0;
+        total += c;
+      }
+    }
+    sc[tid] = tid < e_count ? total : 0;
+    __syncthreads();
+    block_inclusive_scan(sc);
+    if (tid < e_count) {
+      row0[tid] = sc[tid] - total + before;
+      if (b == 0) {
+        counts[tid] = total;
+        offsets[tid + 1] = sc[tid];
+      }
+    }
+    if (b == 0 && tid == 0) offsets[0] = 0;
+  } else {
+    if (tid < e_count) row0[tid] = offsets[tid] + ws.base[b * e_count + tid];
+  }
+  __syncthreads();
   const int64_t t = b * kBlockTok + tid;
+  int ex[8];  // k <= 8; slots past k stay -1 (not local)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = -1;
+    if (t < T && j < k) {
+      ex[j] = idx[t * k + j] - e_begin;
+      if (ex[j] >= 0 && ex[j] < e_count) atomicOr(&m[wave][ex[j]], 1ull << lane);
+    }
+  }
+  __syncthreads();
   if (t >= T) return;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j] - e_begin;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const int e = ex[j];
     int pos = -1;
     if (e >= 0 && e < e_count) {
-      pos = offsets[e] + ws.base[b * e_count + e];
-      for (int w = 0; w < wave; ++w) pos += __popcll(ws.masks[(b * kWaves + w) * e_count + e]);
-      pos += __popcll(ws.masks[(b * kWaves + wave) * e_count + e] & below);
+      pos = row0[e] + __popcll(m[wave][e] & below);
+      for (int w = 0; w < wave; ++w) pos += __popcll(m[w][e]);
       src_token[pos] = static_cast<int32_t>(t);
     }
     inv_pos[t * k + j] = pos;
@@ -178,13 +231,19 @@ void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_cou
                     hipStream_t s) {
   const int64_t B = (T + kBlockTok - 1) / kBlockTok;
   Workspace ws = carve(workspace, B, e_count);
+  const dim3 grid(static_cast<unsigned>(B));
   if (B > 0)
-    permute_mask_kernel<<<dim3(static_cast<unsigned>(B)), 256, 0, s>>>(idx, T, k, e_begin,
-                                                                       e_count, ws);
-  permute_scan_kernel<<<1, 256, 0, s>>>(B, e_count, ws, counts, offsets);
-  if (B > 0)
-    permute_scatter_kernel<<<dim3(static_cast<unsigned>(B)), 256, 0, s>>>(
-        idx, T, k, e_begin, e_count, ws, offsets, src_token, inv_pos);
+    permute_count_kernel<<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, ws);
+  if (B > 0 && B * e_count <= kSelfScanMax) {
+    permute_place_kernel<true><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, B, ws, counts,
+                                                    offsets, src_token, inv_pos);
+  } else {
+    // also for T == 0: zero counts and offsets
+    permute_scan_kernel<<<1, 256, 0, s>>>(B, e_count, ws, counts, offsets);
+    if (B > 0)
+      permute_place_kernel<false><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, B, ws,
+                                                       counts, offsets, src_token, inv_pos);
+  }
   if (x != nullptr && B > 0) {
     const int64_t max_rows = T * k;
     const int64_t items = max_rows * (row_bytes / 16);

@@ -115,6 +115,23 @@ def test_permute(g, T, eb, ec):
     assert torch.equal(xp, x.cpu()[torch.from_numpy(src)])
 
 
+@pytest.mark.parametrize("T,E,k,eb,ec", [
+    (20000, 256, 8, 0, 256),   # 79 blocks x 256 experts: count table scanned in its own pass
+    (16384, 256, 8, 0, 256),   # 64 x 256: the largest table each block scans itself
+    (700, 48, 6, 5, 30),       # k below 8
+])
+def test_permute_block_prefix_paths(g, T, E, k, eb, ec):
+    idx = routing_ids(T, E, k, seed=T + k)
+    res = g.moe_permute(idx, eb, ec, None)
+    torch.cuda.synchronize()
+    counts, offsets, src, inv, _ = oracle.permute(to_i64(idx), eb, ec)
+    S = int(offsets[-1])
+    assert np.array_equal(to_i64(res.counts), counts)
+    assert np.array_equal(to_i64(res.offsets), offsets)
+    assert np.array_equal(to_i64(res.src_token)[:S], src)
+    assert np.array_equal(to_i64(res.inv_pos), inv)
+
+
 def test_permute_f32_rows_and_index_only(g):
     T, E, k, d = 300, 32, 8, 20  # 80-byte f32 rows
     idx = routing_ids(T, E, k, seed=5)
