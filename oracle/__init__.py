@@ -23,7 +23,10 @@ Pages cited (by title, section and equation):
        MLP simulations.
   [P5] "「赤兔」Chitu 框架深度解读（七）：混合专家模型 (MoE) 的高效处理": token
        dispatchers, expert computation (tokens laid out contiguously by expert
-       id), quantisation support (block fp8).
+       id; FP8 GEMMs for prefill), quantisation support (block fp8).
+
+``quant`` holds the fp8-activation side of the block-fp8 prefill variant
+(per-token 1x128 activation groups, READINGS R28 and R29).
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (library cross-checks, closed forms, brute force,
@@ -48,4 +51,12 @@ from .ffn import (  # noqa: F401
     experts,
     combine,
     moe_ffn,
+)
+from .quant import (  # noqa: F401
+    e4m3fn_encode,
+    bf16_round,
+    quantize_rows,
+    dequant_rows,
+    swiglu_a8,
+    experts_a8,
 )
