@@ -29,7 +29,8 @@ _lib.load()  # fail loudly at import if the HIP library is missing
 __all__ = [
     "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "moe_route_workspace_size",
     "moe_route",
-    "moe_permute_workspace_size", "moe_permute",
+    "moe_permute_workspace_size", "moe_permute", "quantize_fp8_rows", "grouped_gate_up_a8",
+    "grouped_down_a8",
     "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
     "version",
 ]
@@ -287,6 +288,71 @@ def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s
     _ok("grouped_down", _lib.load().grouped_down(
         _p(h), _p(offsets), e_count, max_rows, f, d, _p(w_down.data), wdt, _p(s_down), _p(y_perm),
         _s(stream)))
+    return y_perm
+
+
+def quantize_fp8_rows(x: torch.Tensor, *, q=None, scales=None, stream=None):
+    """Per-token 1x128-group E4M3FN codes of bf16 rows. Returns (q uint8 [rows, K],
+    scales f32 [rows, K/128])."""
+    rows, K = x.shape
+    if x.dtype != torch.bfloat16:
+        raise ValueError("quantize_fp8_rows: x must be bf16")
+    if q is None:
+        q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, max(K // 128, 0)), dtype=torch.float32, device=x.device)
+    _dev(x, q, scales)
+    _ok("quantize_fp8_rows", _lib.load().quantize_fp8_rows(_p(x), rows, K, _p(q), _p(scales),
+                                                           _s(stream)))
+    return q, scales
+
+
+def _a8_weights(name, *ws):
+    ws = [_pw(w, name) for w in ws]
+    if any(w.dtype != torch.float8_e4m3fn for w in ws):
+        raise ValueError(f"{name}: weights must be packed float8_e4m3fn codes")
+    return ws
+
+
+def grouped_gate_up_a8(xq: torch.Tensor, x_scale: torch.Tensor, offsets: torch.Tensor,
+                       w_gate, w_up, s_gate: torch.Tensor, s_up: torch.Tensor, *,
+                       row_index=None, h_out=None, stream=None) -> torch.Tensor:
+    """grouped_gate_up with fp8 activations (xq codes + x_scale per 1x128 group).
+    Returns h_out bf16 [max_rows, f]."""
+    max_rows, src_rows = _grouped_rows(xq, row_index, "grouped_gate_up_a8")
+    d = xq.shape[1]
+    w_gate, w_up = _a8_weights("grouped_gate_up_a8", w_gate, w_up)
+    e_count, f = w_gate.groups, w_gate.N
+    if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
+        raise ValueError("grouped_gate_up_a8: w_gate/w_up [E, f, d]")
+    if xq.dtype != torch.uint8 or x_scale.shape != (xq.shape[0], d // 128):
+        raise ValueError("grouped_gate_up_a8: xq uint8 [rows, d], x_scale [rows, d/128]")
+    if h_out is None:
+        h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=xq.device)
+    _dev(xq, x_scale, row_index, offsets, s_gate, s_up, h_out)
+    _ok("grouped_gate_up_a8", _lib.load().grouped_gate_up_a8(
+        _p(xq), _p(x_scale), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
+        _p(w_gate.data), _p(w_up.data), _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
+    return h_out
+
+
+def grouped_down_a8(hq: torch.Tensor, h_scale: torch.Tensor, offsets: torch.Tensor, w_down,
+                    s_down: torch.Tensor, *, y_perm=None, stream=None) -> torch.Tensor:
+    """grouped_down with fp8 activations (hq codes + h_scale per 1x128 group).
+    Returns y_perm bf16 [max_rows, d]."""
+    max_rows, f = hq.shape
+    (w_down,) = _a8_weights("grouped_down_a8", w_down)
+    e_count, d = w_down.groups, w_down.N
+    if w_down.K != f:
+        raise ValueError("grouped_down_a8: w_down [E, d, f]")
+    if hq.dtype != torch.uint8 or h_scale.shape != (max_rows, f // 128):
+        raise ValueError("grouped_down_a8: hq uint8 [rows, f], h_scale [rows, f/128]")
+    if y_perm is None:
+        y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=hq.device)
+    _dev(hq, h_scale, offsets, s_down, y_perm)
+    _ok("grouped_down_a8", _lib.load().grouped_down_a8(
+        _p(hq), _p(h_scale), _p(offsets), e_count, max_rows, f, d, _p(w_down.data), _p(s_down),
+        _p(y_perm), _s(stream)))
     return y_perm
 
 

@@ -215,6 +215,70 @@ int grouped_swiglu(const void* x, const int32_t* row_index, int64_t src_rows,
   return finish();
 }
 
+int quantize_fp8_rows(const void* x, int64_t rows, int32_t K, void* q, float* scales,
+                      void* stream) {
+  if (rows < 0 || K <= 0) return MF_EINVAL;
+  if (K % 128 != 0 || rows > kI32Max) return MF_EUNSUPPORTED;
+  if (rows == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!x || !q || !scales) return MF_EINVAL;
+  if (!a16(x) || reinterpret_cast<uintptr_t>(q) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+    return MF_EUNSUPPORTED;
+  mf::launch_quantize_rows(x, rows, K, q, scales, S(stream));
+  return finish();
+}
+
+namespace {
+
+int check_a8(const void* a, const float* a_scale, const int32_t* offsets, int32_t e_count,
+             int64_t max_rows, int32_t K, int32_t N, const void* w0, const void* w1,
+             const float* s0, const float* s1, const void* out, bool* empty,
+             const int32_t* row_index = nullptr, int64_t src_rows = 0) {
+  *empty = false;
+  if (!offsets || !w0 || !w1 || !s0 || !s1) return MF_EINVAL;
+  if (e_count < 1 || max_rows < 0 || K <= 0 || N <= 0) return MF_EINVAL;
+  if (row_index && (src_rows < 1 || src_rows > kI32Max)) return MF_EINVAL;
+  if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
+  if (K % 256 != 0 || N % 256 != 0) return MF_EUNSUPPORTED;
+  if (max_rows == 0) {  // zero-size buffers may be NULL
+    *empty = true;
+    return MF_OK;
+  }
+  if (!a || !a_scale || !out) return MF_EINVAL;
+  if (!a16(a) || !a16(w0) || !a16(w1) || !a16(out) ||
+      reinterpret_cast<uintptr_t>(a_scale) % 4 != 0)
+    return MF_EUNSUPPORTED;
+  return MF_OK;
+}
+
+}  // namespace
+
+int grouped_gate_up_a8(const void* xq, const float* x_scale, const int32_t* row_index,
+                       int64_t src_rows, const int32_t* offsets, int32_t e_count,
+                       int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
+                       const void* w_up, const float* s_gate, const float* s_up, void* h_out,
+                       void* stream) {
+  bool empty;
+  const int st = check_a8(xq, x_scale, offsets, e_count, max_rows, d, f, w_gate, w_up, s_gate,
+                          s_up, h_out, &empty, row_index, src_rows);
+  if (st != MF_OK || empty) return st;
+  mf::launch_gemm_gateup_a8(xq, x_scale, row_index, src_rows, offsets, e_count, max_rows, d, f,
+                            w_gate, w_up, s_gate, s_up, h_out, num_cus(), S(stream));
+  return finish();
+}
+
+int grouped_down_a8(const void* hq, const float* h_scale, const int32_t* offsets,
+                    int32_t e_count, int64_t max_rows, int32_t f, int32_t d, const void* w_down,
+                    const float* s_down, void* y_perm, void* stream) {
+  bool empty;
+  const int st = check_a8(hq, h_scale, offsets, e_count, max_rows, f, d, w_down, w_down, s_down,
+                          s_down, y_perm, &empty);
+  if (st != MF_OK || empty) return st;
+  mf::launch_gemm_down_a8(hq, h_scale, offsets, e_count, max_rows, f, d, w_down, s_down, y_perm,
+                          num_cus(), S(stream));
+  return finish();
+}
+
 int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w, int64_t T,
                 int32_t k, int32_t d, int64_t max_rows, const void* residual, void* out,
                 int32_t out_dtype, void* stream) {

@@ -53,6 +53,21 @@ void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
                           int64_t max_rows, int K, int N, const void* w_down,
                           const float* s_down, void* y, int num_cus, hipStream_t s);
 
+// fp8 activations ([rows, K] codes + [rows, K/128] f32 group scales) against
+// block-fp8 weights on the fp8 MFMA; bf16 out (gate/up: SiLU(g) * u).
+void launch_gemm_gateup_a8(const void* a, const float* a_scale, const int32_t* a_rows,
+                           int64_t a_src_rows, const int32_t* offsets, int e_count,
+                           int64_t max_rows, int K, int N, const void* w_gate, const void* w_up,
+                           const float* s_gate, const float* s_up, void* h, int num_cus,
+                           hipStream_t s);
+void launch_gemm_down_a8(const void* a, const float* a_scale, const int32_t* offsets,
+                         int e_count, int64_t max_rows, int K, int N, const void* w_down,
+                         const float* s_down, void* y, int num_cus, hipStream_t s);
+
+// per-token 1x128-group E4M3FN quantisation of bf16 rows
+void launch_quantize_rows(const void* x, int64_t rows, int K, void* q, float* scales,
+                          hipStream_t s);
+
 void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w,
                     int64_t T, int k, int d, int64_t max_rows, const void* residual,
                     void* out, bool out_f32, hipStream_t s);

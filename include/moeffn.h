@@ -227,6 +227,60 @@ int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
                  int32_t w_dtype, const float* s_down, void* y_perm, void* stream);
 
 /*
+ * quantize_fp8_rows - per-token fp8 activations for the block-fp8 prefill
+ * variant ("「赤兔」Chitu 框架深度解读（七）：MoE", 专家计算实现: prefill experts run as
+ * FP8 GEMMs on tokens laid out contiguously by expert; 量化支持: block fp8).
+ * Each row of x is cut into groups of 128 consecutive channels; a group's
+ * scale is s = max(amax, 1e-4) / 448 and each element's code is the E4M3FN
+ * value nearest to x / s (ties to even), both in fp32 with IEEE division.
+ *
+ * x       [rows, K] bf16 (16-byte aligned)
+ * q       [rows, K] E4M3FN codes (8-byte aligned)     out
+ * scales  [rows, K/128] f32                            out
+ * Requires K % 128 == 0. rows == 0 is a no-op.
+ */
+int quantize_fp8_rows(const void* x, int64_t rows, int32_t K, void* q, float* scales,
+                      void* stream);
+
+/*
+ * grouped_gate_up_a8 - grouped_gate_up with fp8 activations on the fp8 MFMA:
+ *   H[o_e:o_{e+1}] = SiLU(X_perm W_gate_e) * (X_perm W_up_e)
+ * with X_perm[t, k] = xq[t, k] * x_scale[t, k/128] (quantize_fp8_rows) and
+ * block-fp8 weights (code * scale per 128x128 block). Same passages as
+ * grouped_swiglu plus quantize_fp8_rows' ([P5] FP8 GEMMs for prefill).
+ *
+ * xq, x_scale  row_index == NULL: [max_rows, d] codes and [max_rows, d/128] f32,
+ *              rows grouped by expert; row_index != NULL: [src_rows, d] and
+ *              [src_rows, d/128] un-permuted, row r of X_perm is row row_index[r]
+ *              (entries clamped to [0, src_rows)): the gather is done in the A load
+ * offsets, e_count, max_rows  as grouped_swiglu
+ * w_gate, w_up [e_count, f, d] E4M3FN codes packed by pack_weights
+ * s_gate, s_up [e_count, f/128, d/128] f32
+ * h_out        [max_rows, f] bf16      out (rows < offsets[e_count])
+ * Each 128-deep block of the contraction is summed exactly on the fp8 MFMA
+ * (fp32 accumulation) and added into the fp32 result scaled by its activation
+ * and weight scales; SiLU(g)*u in fp32 in the epilogue.
+ * Requires 1 <= e_count <= 256, d % 256 == 0, f % 256 == 0.
+ */
+int grouped_gate_up_a8(const void* xq, const float* x_scale, const int32_t* row_index,
+                       int64_t src_rows, const int32_t* offsets, int32_t e_count,
+                       int64_t max_rows, int32_t d, int32_t f, const void* w_gate,
+                       const void* w_up, const float* s_gate, const float* s_up, void* h_out,
+                       void* stream);
+
+/*
+ * grouped_down_a8 - grouped_down with fp8 activations on the fp8 MFMA:
+ *   Y_perm[o_e:o_{e+1}] = H W_down_e, H[t, k] = hq[t, k] * h_scale[t, k/128]
+ * hq [max_rows, f] codes and h_scale [max_rows, f/128] f32 (quantize_fp8_rows
+ * of grouped_gate_up_a8's bf16 H), w_down [e_count, d, f] packed E4M3FN codes,
+ * s_down [e_count, d/128, f/128] f32, y_perm [max_rows, d] bf16 out.
+ * Same requirements as grouped_gate_up_a8.
+ */
+int grouped_down_a8(const void* hq, const float* h_scale, const int32_t* offsets,
+                    int32_t e_count, int64_t max_rows, int32_t f, int32_t d, const void* w_down,
+                    const float* s_down, void* y_perm, void* stream);
+
+/*
  * moe_combine - out[t] = sum_{j : inv_pos[t,j] >= 0} topk_w[t,j] * y_perm[inv_pos[t,j]]
  *                        (+ residual[t]).
  * The optional residual is the Pre-Norm block's skip connection ("推理计算流梳理",

@@ -147,3 +147,41 @@ def test_combine_and_shard_validation(lib):
     assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 128, BF16, P, P, N) == MF_EUNSUPPORTED
     assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 256, FP8, P, P, N) == MF_EINVAL
     assert lib.tp_shard_mlp(P, P, P, P, 0, 64, 64, F32, P, P, N) == MF_OK
+
+
+def test_fp8_prefill_validation(lib):
+    # quantize_fp8_rows(x, rows, K, q, scales, stream)
+    assert lib.quantize_fp8_rows(N, 4, 256, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, -1, 256, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, 4, 0, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, 4, 192, P, P, N) == MF_EUNSUPPORTED       # K % 128
+    assert lib.quantize_fp8_rows(ctypes.c_void_p(0x100008), 4, 256, P, P, N) == MF_EUNSUPPORTED
+    assert lib.quantize_fp8_rows(N, 0, 256, N, N, N) == MF_OK                 # zero rows
+
+    def gu(**kw):
+        a = dict(xq=P, xs=P, ri=N, src=0, off=P, ec=4, rows=64, d=256, f=256, wg=P, wu=P,
+                 sg=P, su=P, h=P)
+        a.update(kw)
+        return lib.grouped_gate_up_a8(a["xq"], a["xs"], a["ri"], a["src"], a["off"], a["ec"],
+                                      a["rows"], a["d"], a["f"], a["wg"], a["wu"], a["sg"],
+                                      a["su"], a["h"], N)
+    assert gu(off=N) == MF_EINVAL
+    assert gu(sg=N) == MF_EINVAL                  # weight scales are required
+    assert gu(ec=0) == MF_EINVAL
+    assert gu(ri=P, src=0) == MF_EINVAL           # row_index needs src_rows >= 1
+    assert gu(xs=N) == MF_EINVAL
+    assert gu(ec=257) == MF_EUNSUPPORTED
+    assert gu(d=384) == MF_EUNSUPPORTED           # d % 256
+    assert gu(f=128) == MF_EUNSUPPORTED           # f % 256
+    assert gu(xq=ctypes.c_void_p(0x100008)) == MF_EUNSUPPORTED
+    assert gu(rows=0, xq=N, xs=N, h=N) == MF_OK   # zero rows: nothing to do
+
+    def dn(**kw):
+        a = dict(hq=P, hs=P, off=P, ec=4, rows=64, f=256, d=256, wd=P, sd=P, y=P)
+        a.update(kw)
+        return lib.grouped_down_a8(a["hq"], a["hs"], a["off"], a["ec"], a["rows"], a["f"], a["d"],
+                                   a["wd"], a["sd"], a["y"], N)
+    assert dn(sd=N) == MF_EINVAL
+    assert dn(y=N) == MF_EINVAL
+    assert dn(f=640) == MF_EUNSUPPORTED
+    assert dn(rows=0, hq=N, hs=N, y=N) == MF_OK
