@@ -291,9 +291,10 @@ def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s
     return y_perm
 
 
-def quantize_fp8_rows(x: torch.Tensor, *, q=None, scales=None, stream=None):
+def quantize_fp8_rows(x: torch.Tensor, *, row_count=None, q=None, scales=None, stream=None):
     """Per-token 1x128-group E4M3FN codes of bf16 rows. Returns (q uint8 [rows, K],
-    scales f32 [rows, K/128])."""
+    scales f32 [rows, K/128]). ``row_count`` (a one-element int32 device tensor,
+    e.g. ``offsets[-1:]``) limits the rows quantised without a host sync."""
     rows, K = x.shape
     if x.dtype != torch.bfloat16:
         raise ValueError("quantize_fp8_rows: x must be bf16")
@@ -301,9 +302,9 @@ def quantize_fp8_rows(x: torch.Tensor, *, q=None, scales=None, stream=None):
         q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, max(K // 128, 0)), dtype=torch.float32, device=x.device)
-    _dev(x, q, scales)
-    _ok("quantize_fp8_rows", _lib.load().quantize_fp8_rows(_p(x), rows, K, _p(q), _p(scales),
-                                                           _s(stream)))
+    _dev(x, row_count, q, scales)
+    _ok("quantize_fp8_rows", _lib.load().quantize_fp8_rows(_p(x), rows, _p(row_count), K, _p(q),
+                                                           _p(scales), _s(stream)))
     return q, scales
 
 
@@ -422,9 +423,17 @@ class MoEFFNLayer:
 
     def __init__(self, *, T: int, d: int, f: int, w_r, bias, w_gate, w_up, w_down,
                  e_begin: int = 0, gamma=None, s_gate=None, s_up=None, s_down=None,
-                 k: int = 8, eps: float = 1e-5, out_dtype=torch.bfloat16):
+                 k: int = 8, eps: float = 1e-5, out_dtype=torch.bfloat16,
+                 act_fp8: bool = False):
         """Weights are given [out, in] (w_r [E, d], w_gate/w_up [E_loc, f, d],
-        w_down [E_loc, d, f]) and packed here, once."""
+        w_down [E_loc, d, f]) and packed here, once.
+
+        ``act_fp8`` (block-fp8 weights only): the expert GEMMs take fp8
+        activations, as the block-fp8 prefill variant does: V is quantised per
+        token and 1x128 group before the gate/up GEMM and H before the down
+        GEMM (quantize_fp8_rows), and the GEMMs run on the fp8 MFMA
+        (grouped_gate_up_a8 / grouped_down_a8). Each quantisation is timed with
+        the GEMM it feeds."""
         dev = w_r.device
         self.T, self.d, self.f, self.k, self.eps = T, d, f, k, eps
         self.e_begin, self.e_count = e_begin, w_gate.shape[0]
@@ -448,6 +457,14 @@ class MoEFFNLayer:
         self.h = torch.empty((rows, f), dtype=bf, device=dev)
         self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
+        self.act_fp8 = act_fp8
+        if act_fp8:
+            if w_gate.dtype != torch.float8_e4m3fn or s_gate is None:
+                raise ValueError("MoEFFNLayer: act_fp8 needs block-fp8 weights and scales")
+            self.vq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.vs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+            self.hq = torch.empty((rows, f), dtype=torch.uint8, device=dev)
+            self.hs = torch.empty((rows, f // 128), dtype=torch.float32, device=dev)
 
     def forward(self, x: torch.Tensor, stream=None, marks=None,
                 residual: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -468,10 +485,22 @@ class MoEFFNLayer:
                     offsets=self.offsets, src_token=self.src_token, inv_pos=self.inv_pos,
                     workspace=self.workspace, stream=s)
         mark(3)
-        grouped_gate_up(v, self.offsets, self.w[0], self.w[1], self.s[0], self.s[1],
-                        row_index=self.src_token, h_out=self.h, stream=s)
-        mark(4)
-        grouped_down(self.h, self.offsets, self.w[2], self.s[2], y_perm=self.y_perm, stream=s)
+        if self.act_fp8:
+            quantize_fp8_rows(v, q=self.vq, scales=self.vs, stream=s)
+            grouped_gate_up_a8(self.vq, self.vs, self.offsets, self.w[0], self.w[1], self.s[0],
+                               self.s[1], row_index=self.src_token, h_out=self.h, stream=s)
+            mark(4)
+            # only the live rows of H (offsets[-1], known on the device)
+            quantize_fp8_rows(self.h, row_count=self.offsets[-1:], q=self.hq, scales=self.hs,
+                              stream=s)
+            grouped_down_a8(self.hq, self.hs, self.offsets, self.w[2], self.s[2],
+                            y_perm=self.y_perm, stream=s)
+        else:
+            grouped_gate_up(v, self.offsets, self.w[0], self.w[1], self.s[0], self.s[1],
+                            row_index=self.src_token, h_out=self.h, stream=s)
+            mark(4)
+            grouped_down(self.h, self.offsets, self.w[2], self.s[2], y_perm=self.y_perm,
+                         stream=s)
         mark(5)
         out = moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out,
                           residual=residual, stream=s)

@@ -215,8 +215,8 @@ int grouped_swiglu(const void* x, const int32_t* row_index, int64_t src_rows,
   return finish();
 }
 
-int quantize_fp8_rows(const void* x, int64_t rows, int32_t K, void* q, float* scales,
-                      void* stream) {
+int quantize_fp8_rows(const void* x, int64_t rows, const int32_t* row_count, int32_t K, void* q,
+                      float* scales, void* stream) {
   if (rows < 0 || K <= 0) return MF_EINVAL;
   if (K % 128 != 0 || rows > kI32Max) return MF_EUNSUPPORTED;
   if (rows == 0) return MF_OK;  // zero-size buffers may be NULL
@@ -224,7 +224,7 @@ int quantize_fp8_rows(const void* x, int64_t rows, int32_t K, void* q, float* sc
   if (!a16(x) || reinterpret_cast<uintptr_t>(q) % 8 != 0 ||
       reinterpret_cast<uintptr_t>(scales) % 4 != 0)
     return MF_EUNSUPPORTED;
-  mf::launch_quantize_rows(x, rows, K, q, scales, S(stream));
+  mf::launch_quantize_rows(x, rows, row_count, K, q, scales, S(stream));
   return finish();
 }
 

@@ -65,8 +65,8 @@ void launch_gemm_down_a8(const void* a, const float* a_scale, const int32_t* off
                          const float* s_down, void* y, int num_cus, hipStream_t s);
 
 // per-token 1x128-group E4M3FN quantisation of bf16 rows
-void launch_quantize_rows(const void* x, int64_t rows, int K, void* q, float* scales,
-                          hipStream_t s);
+void launch_quantize_rows(const void* x, int64_t rows, const int32_t* row_count, int K, void* q,
+                          float* scales, hipStream_t s);
 
 void launch_combine(const void* y_perm, const int32_t* inv_pos, const float* w,
                     int64_t T, int k, int d, int64_t max_rows, const void* residual,

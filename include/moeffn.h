@@ -234,13 +234,17 @@ int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
  * scale is s = max(amax, 1e-4) / 448 and each element's code is the E4M3FN
  * value nearest to x / s (ties to even), both in fp32 with IEEE division.
  *
- * x       [rows, K] bf16 (16-byte aligned)
- * q       [rows, K] E4M3FN codes (8-byte aligned)     out
- * scales  [rows, K/128] f32                            out
+ * x          [rows, K] bf16 (16-byte aligned)
+ * row_count  NULL, or a device int32: only rows [0, min(*row_count, rows)) are
+ *            quantised and the rest of q / scales is left untouched (e.g.
+ *            offsets + e_count for a grouped H, whose live rows are known only
+ *            on the device)
+ * q          [rows, K] E4M3FN codes (8-byte aligned)     out
+ * scales     [rows, K/128] f32                            out
  * Requires K % 128 == 0. rows == 0 is a no-op.
  */
-int quantize_fp8_rows(const void* x, int64_t rows, int32_t K, void* q, float* scales,
-                      void* stream);
+int quantize_fp8_rows(const void* x, int64_t rows, const int32_t* row_count, int32_t K, void* q,
+                      float* scales, void* stream);
 
 /*
  * grouped_gate_up_a8 - grouped_gate_up with fp8 activations on the fp8 MFMA:

@@ -352,7 +352,7 @@ def combine(y_perm, inv_pos, w, residual=None) -> np.ndarray:
 
 
 def moe_ffn(x, gamma, w_r, bias, weights, e_begin: int, e_count: int,
-            k: int = 8, eps: float = 1e-5, norm: bool = True, idx=None):
+            k: int = 8, eps: float = 1e-5, norm: bool = True, idx=None, act_fp8: bool = False):
     """One rank's share of the MoE FFN sub-block, ``FFN(RMSNorm(x))``.
 
     Steps in the pages' order: RMSNorm ([P1] Norm&Residual) -> router ([P1]
@@ -362,7 +362,9 @@ def moe_ffn(x, gamma, w_r, bias, weights, e_begin: int, e_count: int,
     ``norm=False`` the router sees x directly (READING R11, the router-only
     workload). ``idx`` optionally fixes the routed sets (the weights are then
     recomputed from the unbiased scores), which the parity checker uses when a
-    token's 8th/9th key gap is below the tie threshold.
+    token's 8th/9th key gap is below the tie threshold. ``act_fp8`` runs the
+    experts with fp8 activations (``quant.experts_a8``, the block-fp8 prefill
+    variant, READINGS R28/R29) on the bf16-held V.
 
     Returns a dict with every intermediate: v, idx, w, s, key, gap, counts,
     offsets, src_token, inv_pos, x_perm, y_perm, out.
@@ -374,7 +376,12 @@ def moe_ffn(x, gamma, w_r, bias, weights, e_begin: int, e_count: int,
         r_idx = np.asarray(idx, dtype=np.int64)
         r_w = route_weights(s, r_idx)
     counts, offsets, src_token, inv_pos, x_perm = permute(r_idx, e_begin, e_count, v)
-    y_perm = experts(x_perm, offsets, weights)
+    if act_fp8:
+        from .quant import bf16_round, experts_a8
+        # the GEMM input V is held in bf16 between RMSNorm and the quantiser
+        y_perm, _ = experts_a8(bf16_round(x_perm), offsets, weights)
+    else:
+        y_perm = experts(x_perm, offsets, weights)
     out = combine(y_perm, inv_pos, r_w)
     return dict(v=v, idx=r_idx, w=r_w, s=s, key=key, gap=gap, counts=counts,
                 offsets=offsets, src_token=src_token, inv_pos=inv_pos,

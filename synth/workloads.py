@@ -13,6 +13,9 @@ the builder functions also take smaller shapes for parity cases.
   moe_prefill_8192tok_32exp_bf16   8192 tokens, d 4096, f 2048, E 256 with the
                                    32 local experts [0,32), bias skewed by
                                    A*(e+1)^-1.1, bf16 experts ~N(0,0.02)
+  moe_prefill_8192tok_32exp_fp8act the prefill shape and routing with the experts
+                                   drawn ~N(0,0.02) f32 then block-fp8 quantised,
+                                   run with fp8 activations (per-token 1x128)
   moe_decode_64tok_256exp_fp8      64 tokens, all 256 experts local, experts
                                    drawn ~N(0,0.02) f32 then block-fp8 quantised
 """
@@ -36,6 +39,9 @@ WORKLOADS = {
     "moe_prefill_8192tok_32exp_bf16": dict(kind="moe", T=8192, d=4096, f=2048,
                                            E=256, e_begin=0, e_count=32,
                                            wdtype="bf16", zipf=ZIPF_AMPLITUDE),
+    "moe_prefill_8192tok_32exp_fp8act": dict(kind="moe", T=8192, d=4096, f=2048,
+                                             E=256, e_begin=0, e_count=32, wdtype="fp8",
+                                             act_fp8=True, zipf=ZIPF_AMPLITUDE),
     "moe_decode_64tok_256exp_fp8": dict(kind="moe", T=64, d=4096, f=2048, E=256,
                                         e_begin=0, e_count=256, wdtype="fp8",
                                         zipf=0.0),

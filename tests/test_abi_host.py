@@ -151,12 +151,12 @@ def test_combine_and_shard_validation(lib):
 
 def test_fp8_prefill_validation(lib):
     # quantize_fp8_rows(x, rows, K, q, scales, stream)
-    assert lib.quantize_fp8_rows(N, 4, 256, P, P, N) == MF_EINVAL
-    assert lib.quantize_fp8_rows(P, -1, 256, P, P, N) == MF_EINVAL
-    assert lib.quantize_fp8_rows(P, 4, 0, P, P, N) == MF_EINVAL
-    assert lib.quantize_fp8_rows(P, 4, 192, P, P, N) == MF_EUNSUPPORTED       # K % 128
-    assert lib.quantize_fp8_rows(ctypes.c_void_p(0x100008), 4, 256, P, P, N) == MF_EUNSUPPORTED
-    assert lib.quantize_fp8_rows(N, 0, 256, N, N, N) == MF_OK                 # zero rows
+    assert lib.quantize_fp8_rows(N, 4, N, 256, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, -1, N, 256, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, 4, N, 0, P, P, N) == MF_EINVAL
+    assert lib.quantize_fp8_rows(P, 4, N, 192, P, P, N) == MF_EUNSUPPORTED       # K % 128
+    assert lib.quantize_fp8_rows(ctypes.c_void_p(0x100008), 4, N, 256, P, P, N) == MF_EUNSUPPORTED
+    assert lib.quantize_fp8_rows(N, 0, N, 256, N, N, N) == MF_OK                 # zero rows
 
     def gu(**kw):
         a = dict(xq=P, xs=P, ri=N, src=0, off=P, ec=4, rows=64, d=256, f=256, wg=P, wu=P,

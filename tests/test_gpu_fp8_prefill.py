@@ -58,6 +58,22 @@ def test_quantize_fp8_rows_bit_exact(g, rows, K):
                           f"{got[tuple(bad[0])]:#x} vs {q_ref[tuple(bad[0])]:#x}"
 
 
+@pytest.mark.parametrize("live", [0, 1, 57, 300, 500])
+def test_quantize_fp8_rows_device_row_count(g, live):
+    # only rows < min(*row_count, rows) are written; the rest keep their contents
+    rows, K = 300, 512
+    x = _rows_with_structure(rows, K, seed=live + 11)
+    q = torch.full((rows, K), 0xA5, dtype=torch.uint8, device=DEV)
+    s = torch.full((rows, K // 128), -1.0, dtype=torch.float32, device=DEV)
+    cnt = torch.tensor([live], dtype=torch.int32, device=DEV)
+    g.quantize_fp8_rows(x, row_count=cnt, q=q, scales=s)
+    torch.cuda.synchronize()
+    n = min(live, rows)
+    q_ref, s_ref = oracle.quantize_rows(to_f64(x[:n])) if n else (np.zeros((0, K)), np.zeros((0, 4)))
+    assert np.array_equal(_codes(q[:n]), q_ref) and np.array_equal(s[:n].double().cpu().numpy(), s_ref)
+    assert (q[n:] == 0xA5).all() and (s[n:] == -1.0).all()
+
+
 def test_quantize_fp8_rows_zero_rows(g):
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
     q, s = g.quantize_fp8_rows(x)

@@ -40,11 +40,11 @@ def g():
     return mod
 
 
-def build_layer(g, inp, T, d, f, e_begin):
+def build_layer(g, inp, T, d, f, e_begin, act_fp8=False):
     return g.MoEFFNLayer(T=T, d=d, f=f, w_r=inp["w_r"], bias=inp["bias"], gamma=inp.get("gamma"),
                          w_gate=inp["w_gate"], w_up=inp["w_up"], w_down=inp["w_down"],
                          e_begin=e_begin, s_gate=inp.get("s_gate"), s_up=inp.get("s_up"),
-                         s_down=inp.get("s_down"))
+                         s_down=inp.get("s_down"), act_fp8=act_fp8)
 
 
 def expert_f64(inp, e, wdtype):
@@ -73,7 +73,14 @@ def weight_rows_f64(inp, key, e, rows, wdtype):
 
 def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
                 col_sample=None, e2e_tokens=None):
-    """Stage-by-stage and end-to-end parity of one forward pass (see module doc)."""
+    """Stage-by-stage and end-to-end parity of one forward pass (see module doc).
+
+    With the layer's fp8 activations (block-fp8 prefill variant) the GEMMs are
+    checked on the GPU's own codes: gate/up on the quantised V rows it
+    gathers, down on the quantised H (whose codes are compared bit for bit
+    with the oracle's quantiser on the GPU's H); end to end against the
+    oracle's fp8-activation sub-block."""
+    a8 = getattr(layer, "act_fp8", False)
     rel = 5e-3 if wdtype == "bf16" else REL_FP8
     out = layer(inp["x"])
     torch.cuda.synchronize()
@@ -103,7 +110,18 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
 
     # expert GEMMs on the gathered rows V[src_token] (H) and the GPU's H
     # (Y_perm): all rows, sampled columns
-    xp = v_gpu[src]
+    if a8:
+        vq = layer.vq.cpu().numpy().astype(np.uint8)
+        xp = oracle.dequant_rows(vq[src], layer.vs.double().cpu().numpy()[src])
+        hq_ref, hs_ref = oracle.quantize_rows(to_f64(layer.h[:S]))
+        assert np.array_equal(layer.hq[:S].cpu().numpy().astype(np.uint8), hq_ref)
+        assert np.array_equal(layer.hs[:S].double().cpu().numpy(), hs_ref)
+        h_in = oracle.dequant_rows(hq_ref, hs_ref)
+        rel_gemm = 5e-3   # each GEMM on its fp8 operands: bf16 output rounding only
+    else:
+        xp = v_gpu[src]
+        h_in = to_f64(layer.h[:S])
+        rel_gemm = rel
     h_gpu = to_f64(layer.h[:S])
     y_gpu = to_f64(layer.y_perm[:S])
     hc = np.arange(f) if col_sample is None else np.asarray(col_sample)
@@ -118,9 +136,9 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
         wu = weight_rows_f64(inp, "w_up", e, list(hc), wdtype)
         wd = weight_rows_f64(inp, "w_down", e, list(yc), wdtype)
         h_ref[a:b] = oracle.silu(xp[a:b] @ wg.T) * (xp[a:b] @ wu.T)
-        y_ref[a:b] = h_gpu[a:b] @ wd.T
-    assert_fp("H", h_gpu[:, hc], h_ref, rel=rel, max_abs=None)
-    assert_fp("Y_perm (from GPU H)", y_gpu[:, yc], y_ref, rel=rel, max_abs=None)
+        y_ref[a:b] = h_in[a:b] @ wd.T
+    assert_fp("H", h_gpu[:, hc], h_ref, rel=rel_gemm, max_abs=None)
+    assert_fp("Y_perm (from GPU H)", y_gpu[:, yc], y_ref, rel=rel_gemm, max_abs=None)
 
     # combine on the GPU's Y_perm
     out_gpu = to_f64(out)
@@ -132,7 +150,7 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
     need = sorted({int(i) - eb for t in et for i in gpu_idx[t] if eb <= i < eb + ec})
     cache = {e: expert_f64(inp, e, wdtype) for e in need}
     ref = oracle.moe_ffn(x[et], to_f64(inp["gamma"]), w_r, bias,
-                         lambda e: cache[e], eb, ec, idx=gpu_idx[et])
+                         lambda e: cache[e], eb, ec, idx=gpu_idx[et], act_fp8=a8)
     max_abs = 2e-2 if wdtype == "bf16" else None
     assert_fp("FFN output (end to end)", out_gpu[et], ref["out"], rel=rel, max_abs=max_abs)
     return dict(S=S, near_ties=n_near)
@@ -145,6 +163,14 @@ def test_moe_ffn_small(g, wdtype, T, eb, ec):
     inp = make_moe(T, d, f, E, eb, ec, wdtype=wdtype, seed=T + ec, device=DEV)
     layer = build_layer(g, inp, T, d, f, eb)
     check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype)
+
+
+@pytest.mark.parametrize("T,eb,ec", [(200, 16, 16), (77, 0, 64), (1, 60, 4)])
+def test_moe_ffn_small_fp8_activations(g, T, eb, ec):
+    d, f, E = 256, 256, 64
+    inp = make_moe(T, d, f, E, eb, ec, wdtype="fp8", seed=T + ec + 3, device=DEV)
+    layer = build_layer(g, inp, T, d, f, eb, act_fp8=True)
+    check_layer(g, layer, inp, T, d, f, E, eb, ec, "fp8")
 
 
 def test_moe_ffn_forced_empty_and_single_expert(g):
@@ -239,3 +265,18 @@ def test_workload_decode_64tok_fp8(g):
                       spec["e_begin"], spec["e_count"], "fp8",
                       col_sample=list(range(256, 288)), e2e_tokens=[0, 63])
     assert res["S"] == 64 * 8
+
+
+def test_workload_prefill_8192tok_fp8_activations(g):
+    spec = WORKLOADS["moe_prefill_8192tok_32exp_fp8act"]
+    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
+                   wdtype="fp8", zipf=spec["zipf"], device=DEV)
+    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"], act_fp8=True)
+    T = spec["T"]
+    r = np.random.default_rng(2)
+    tokens = np.sort(r.choice(T, size=128, replace=False))
+    tokens[0], tokens[-1] = 0, T - 1
+    res = check_layer(g, layer, inp, T, spec["d"], spec["f"], spec["E"], spec["e_begin"],
+                      spec["e_count"], "fp8", token_sample=tokens,
+                      col_sample=list(range(128, 160)) + [2047], e2e_tokens=tokens[:6])
+    assert res["S"] == to_i64(layer.counts).sum()
