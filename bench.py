@@ -32,8 +32,10 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE FFN tokens/s per layer on 1 GPU; grouped-GEMM % MFMA peak; decode % HBM BW"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PREFILL = "moe_prefill_8192tok_32exp_bf16"
 DECODE = "moe_decode_64tok_256exp_fp8"
+PREFILL_FP8 = "moe_prefill_8192tok_32exp_fp8act"
 DENSE = "norm_tp_shard_bf16_4096"
 ROUTER = "router_4096tok_E256"
 
@@ -49,8 +51,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the decode / dense-shard / router-only measurements")
-    ap.add_argument("--only", choices=["prefill", "decode", "dense", "router"], default=None,
+                    help="skip the decode / fp8-activation prefill / dense-shard / router-only "
+                         "measurements")
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "router", "prefill_fp8"],
+                    default=None,
                     help="run one workload only (for profiling); prints its stage times")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first copy a 1 GiB device buffer 3 times (a kernel of "
@@ -61,9 +65,20 @@ def parse():
 # ----------------------------------------------------------------- work model
 
 
-def moe_work(T, d, f, E, k, S, active, ec, welt):
-    """Algorithmic bytes / flops per stage of one MoE FFN step (each tensor once)."""
+def moe_work(T, d, f, E, k, S, active, ec, welt, act_fp8=False):
+    """Algorithmic bytes / flops per stage of one MoE FFN step (each tensor once).
+
+    With fp8 activations the gate/up stage also quantises V (read 2d, write
+    d + d/32 bytes per token) and reads the fp8 rows, and the down stage
+    quantises the live rows of H and reads them as fp8."""
     sc = 0 if welt == 2 else 4 * (f // 128) * (d // 128)  # fp8 scales per matrix
+    if act_fp8:
+        w = moe_work(T, d, f, E, k, S, active, ec, welt)
+        w["grouped_gate_up"]["bytes"] = (active * (2 * f * d + 2 * sc) + T * d * 2 + T * d
+                                         + T * d // 32 + S * d + S * d // 32 + S * f * 2 + S * 4)
+        w["grouped_down"]["bytes"] = (active * (d * f + sc) + S * f * 2 + S * f + S * f // 32
+                                      + S * f + S * f // 32 + S * d * 2)
+        return w
     return {
         "rmsnorm": dict(bytes=2 * T * d * 2 + d * 2),
         "moe_route": dict(bytes=T * d * 2 + E * d * 2 + E * 4 + T * k * 8, flops=2 * T * d * E),
@@ -101,7 +116,7 @@ def measured_traffic(kernel: str, profile: str):
     return None
 
 
-def stage_report(work, us):
+def stage_report(work, us, mfma_peak=PEAK_BF16_TFLOPS):
     out = {}
     for name, w in work.items():
         t = us[name] * 1e-6
@@ -111,7 +126,7 @@ def stage_report(work, us):
             r.update(gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
         if "flops" in w:
             tf = w["flops"] / t / 1e12
-            r.update(tflop_s=round(tf, 1), mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4))
+            r.update(tflop_s=round(tf, 1), mfma_frac=round(tf / mfma_peak, 4))
         out[name] = r
     return out
 
@@ -153,7 +168,7 @@ def build_layer(spec, device, seed=0):
                           bias=inp["bias"], gamma=inp["gamma"], w_gate=inp["w_gate"],
                           w_up=inp["w_up"], w_down=inp["w_down"], e_begin=spec["e_begin"],
                           s_gate=inp.get("s_gate"), s_up=inp.get("s_up"),
-                          s_down=inp.get("s_down"))
+                          s_down=inp.get("s_down"), act_fp8=spec.get("act_fp8", False))
     return layer, inp
 
 
@@ -169,7 +184,7 @@ def run_moe(name, steps, warmup):
     counts = layer.counts.cpu()
     welt = 2 if spec["wdtype"] == "bf16" else 1
     work = moe_work(spec["T"], spec["d"], spec["f"], spec["E"], 8, S, active, spec["e_count"],
-                    welt)
+                    welt, act_fp8=spec.get("act_fp8", False))
     log(f"[bench] {name}: {ms * 1e3:.1f} us/step, S={S}, active experts {active}")
     info = dict(slots=S, active_experts=active,
                 count_min=int(counts.min()), count_max=int(counts.max()),
@@ -332,10 +347,12 @@ def main():
             torch.cuda.synchronize()
             del src, dst
             log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
-        if args.only in ("prefill", "decode"):
-            res = run_moe(PREFILL if args.only == "prefill" else DECODE, args.steps, args.warmup)
+        if args.only in ("prefill", "decode", "prefill_fp8"):
+            name = {"prefill": PREFILL, "decode": DECODE, "prefill_fp8": PREFILL_FP8}[args.only]
+            res = run_moe(name, args.steps, args.warmup)
+            peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
-                                  stages=stage_report(res["work"], res["us"]), **res["info"]),
+                                  stages=stage_report(res["work"], res["us"], peak), **res["info"]),
                              default=str), flush=True)
         elif args.only == "dense":
             print(json.dumps(run_dense(args.steps, args.warmup)), flush=True)
@@ -393,6 +410,17 @@ def main():
                               gemm_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                           "stages": dstage}
         del dec
+        torch.cuda.empty_cache()
+        p8 = run_moe(PREFILL_FP8, max(10, args.steps // 2), args.warmup)
+        gw = p8["work"]["grouped_gate_up"]["flops"] + p8["work"]["grouped_down"]["flops"]
+        gus = p8["us"]["grouped_gate_up"] + p8["us"]["grouped_down"]
+        line["prefill_fp8_activations"] = {
+            "workload": PREFILL_FP8, "tokens_per_s": round(T / (p8["ms"] * 1e-3), 1),
+            "ms_per_step": round(p8["ms"], 4), **p8["info"],
+            # the GEMM stages include the activation quantisation that feeds them
+            "grouped_gemm_fp8_mfma_frac": round(gw / (gus * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "stages": stage_report(p8["work"], p8["us"], PEAK_FP8_TFLOPS)}
+        del p8
         torch.cuda.empty_cache()
         line["dense_shard"] = run_dense(max(10, args.steps // 2), args.warmup)
         line["router_only"] = run_router(max(10, args.steps // 2), args.warmup)
