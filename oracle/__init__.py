@@ -26,7 +26,7 @@ Pages cited (by title, section and equation):
        id; FP8 GEMMs for prefill), quantisation support (block fp8).
 
 ``quant`` holds the fp8-activation side of the block-fp8 prefill variant
-(per-token 1x128 activation groups, READINGS R28 and R29).
+(per-token 1x128 activation groups, READINGS R32 and R33).
 
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle_*.py`` (library cross-checks, closed forms, brute force,

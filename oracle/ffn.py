@@ -364,7 +364,7 @@ def moe_ffn(x, gamma, w_r, bias, weights, e_begin: int, e_count: int,
     recomputed from the unbiased scores), which the parity checker uses when a
     token's 8th/9th key gap is below the tie threshold. ``act_fp8`` runs the
     experts with fp8 activations (``quant.experts_a8``, the block-fp8 prefill
-    variant, READINGS R28/R29) on the bf16-held V.
+    variant, READINGS R32/R33) on the bf16-held V.
 
     Returns a dict with every intermediate: v, idx, w, s, key, gap, counts,
     offsets, src_token, inv_pos, x_perm, y_perm, out.

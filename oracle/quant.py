@@ -9,14 +9,14 @@ and quantised experts follow the block-fp8 scheme (量化支持, blockfp8). The 
 name the scheme but do not spell out the activation side; the readings used
 here (also listed in the design document):
 
-READING R28: a linear layer with block-fp8 weights quantises its bf16 input
+READING R32: a linear layer with block-fp8 weights quantises its bf16 input
   per token and per group of 128 consecutive input channels: the group scale
   is ``s = max(amax, 1e-4) / 448`` and the code is the E4M3FN value nearest to
   ``x / s`` (ties to even, saturating at 448). Scale and quotient are computed
   in float32 (the precision both sides take the code decision in).
-READING R29: between the two linear layers of an expert the intermediate
+READING R33: between the two linear layers of an expert the intermediate
   ``H = SiLU(X W_gate) * (X W_up)`` is held in bf16 (as in the bf16 path) and
-  is quantised by R28 as the down projection's input.
+  is quantised by R32 as the down projection's input.
 
 Weights keep their own 128x128 block scales (READING R21, ``dequant_block_fp8``).
 Every product of dequantised values below is exact float64 arithmetic.
@@ -62,7 +62,7 @@ def bf16_round(x) -> np.ndarray:
 
 
 def quantize_rows(x, group: int = 128):
-    """READING R28 on the rows of ``x`` ([rows, K], values exact in float32):
+    """READING R32 on the rows of ``x`` ([rows, K], values exact in float32):
     returns ``(codes uint8 [rows, K], scales float64 [rows, K/group])``.
 
     Per group: ``amax`` (exact), ``s = fl32(max(amax, 1e-4) / 448)``, then the
@@ -87,7 +87,7 @@ def dequant_rows(codes, scales, group: int = 128) -> np.ndarray:
 
 
 def swiglu_a8(x, w_gate, w_up, w_down):
-    """One expert's gated MLP with fp8 activations (READINGS R28, R29).
+    """One expert's gated MLP with fp8 activations (READINGS R32, R33).
 
     ``x`` [m, d] (bf16 values); weights dequantised float64 in the pages'
     orientation (``[d, f]``, ``[d, f]``, ``[f, d]``). Returns ``(y, h)`` with
