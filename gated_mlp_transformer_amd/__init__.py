@@ -29,7 +29,8 @@ _lib.load()  # fail loudly at import if the HIP library is missing
 __all__ = [
     "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "moe_route_workspace_size",
     "moe_route",
-    "moe_permute_workspace_size", "moe_permute", "quantize_fp8_rows", "grouped_gate_up_a8",
+    "moe_permute_workspace_size", "moe_permute", "moe_dispatch_masked", "MaskedDispatch",
+    "grouped_gate_up_masked", "grouped_down_masked", "quantize_fp8_rows", "grouped_gate_up_a8",
     "grouped_down_a8",
     "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
     "version",
@@ -200,6 +201,74 @@ def moe_permute(topk_idx: torch.Tensor, e_begin: int, e_count: int,
         _p(offsets), _p(src_token), _p(inv_pos), _p(workspace),
         workspace.numel() * workspace.element_size(), _s(stream)))
     return PermuteResult(counts, offsets, src_token, inv_pos, x_perm)
+
+
+class MaskedDispatch(NamedTuple):
+    counts: torch.Tensor     # [e_count] int32: rows used per expert block
+    row_index: torch.Tensor  # [e_count * cap] int32: token of each used row
+    pos: torch.Tensor        # [T, k] int32: row of each slot or -1
+    cap: int
+
+
+def moe_dispatch_masked(topk_idx: torch.Tensor, e_begin: int, e_count: int, cap: int, *,
+                        counts=None, row_index=None, pos=None, workspace=None,
+                        stream=None) -> MaskedDispatch:
+    """Masked (fixed-capacity) layout: slot (t, j) of local expert e -> row e*cap + rank."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    i32 = torch.int32
+    counts = torch.empty(e_count, dtype=i32, device=dev) if counts is None else counts
+    row_index = torch.empty(e_count * cap, dtype=i32, device=dev) if row_index is None else row_index
+    pos = torch.empty((T, k), dtype=i32, device=dev) if pos is None else pos
+    need = moe_permute_workspace_size(T, k, e_count)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(topk_idx, counts, row_index, pos, workspace)
+    if topk_idx.dtype != i32:
+        raise ValueError("moe_dispatch_masked: topk_idx must be int32")
+    _ok("moe_dispatch_masked", _lib.load().moe_dispatch_masked(
+        _p(topk_idx), T, k, e_begin, e_count, cap, _p(counts), _p(row_index), _p(pos),
+        _p(workspace), workspace.numel() * workspace.element_size(), _s(stream)))
+    return MaskedDispatch(counts, row_index, pos, cap)
+
+
+def grouped_gate_up_masked(x: torch.Tensor, row_index: torch.Tensor, counts: torch.Tensor,
+                           cap: int, w_gate, w_up, s_gate=None, s_up=None, *, h_out=None,
+                           stream=None) -> torch.Tensor:
+    """grouped_gate_up over the masked layout (rows V[row_index], blocks of cap). Returns h_out."""
+    src_rows, d = x.shape
+    w_gate, w_up = _pw(w_gate, "grouped_gate_up_masked"), _pw(w_up, "grouped_gate_up_masked")
+    e_count, f = w_gate.groups, w_gate.N
+    if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
+        raise ValueError("grouped_gate_up_masked: w_gate/w_up [E, f, d]")
+    if row_index.numel() != e_count * cap or counts.numel() != e_count:
+        raise ValueError("grouped_gate_up_masked: row_index [E*cap], counts [E]")
+    wdt = _grouped_dtype(w_gate, w_up)
+    if h_out is None:
+        h_out = torch.empty((e_count * cap, f), dtype=torch.bfloat16, device=x.device)
+    _dev(x, row_index, counts, s_gate, s_up, h_out)
+    _ok("grouped_gate_up_masked", _lib.load().grouped_gate_up_masked(
+        _p(x), _p(row_index), src_rows, _p(counts), cap, e_count, d, f, _p(w_gate.data),
+        _p(w_up.data), wdt, _p(s_gate), _p(s_up), _p(h_out), _s(stream)))
+    return h_out
+
+
+def grouped_down_masked(h: torch.Tensor, counts: torch.Tensor, cap: int, w_down, s_down=None, *,
+                        y_perm=None, stream=None) -> torch.Tensor:
+    """grouped_down over the masked layout. Returns y_perm [E*cap, d]."""
+    rows, f = h.shape
+    w_down = _pw(w_down, "grouped_down_masked")
+    e_count, d = w_down.groups, w_down.N
+    if w_down.K != f or rows != e_count * cap:
+        raise ValueError("grouped_down_masked: h [E*cap, f], w_down [E, d, f]")
+    wdt = _grouped_dtype(w_down)
+    if y_perm is None:
+        y_perm = torch.empty((rows, d), dtype=torch.bfloat16, device=h.device)
+    _dev(h, counts, s_down, y_perm)
+    _ok("grouped_down_masked", _lib.load().grouped_down_masked(
+        _p(h), _p(counts), cap, e_count, f, d, _p(w_down.data), wdt, _p(s_down), _p(y_perm),
+        _s(stream)))
+    return y_perm
 
 
 def _grouped_rows(x: torch.Tensor, row_index, name: str):
@@ -424,7 +493,7 @@ class MoEFFNLayer:
     def __init__(self, *, T: int, d: int, f: int, w_r, bias, w_gate, w_up, w_down,
                  e_begin: int = 0, gamma=None, s_gate=None, s_up=None, s_down=None,
                  k: int = 8, eps: float = 1e-5, out_dtype=torch.bfloat16,
-                 act_fp8: bool = False):
+                 act_fp8: bool = False, layout: str = "contiguous", cap: Optional[int] = None):
         """Weights are given [out, in] (w_r [E, d], w_gate/w_up [E_loc, f, d],
         w_down [E_loc, d, f]) and packed here, once.
 
@@ -433,7 +502,13 @@ class MoEFFNLayer:
         token and 1x128 group before the gate/up GEMM and H before the down
         GEMM (quantize_fp8_rows), and the GEMMs run on the fp8 MFMA
         (grouped_gate_up_a8 / grouped_down_a8). Each quantisation is timed with
-        the GEMM it feeds."""
+        the GEMM it feeds.
+
+        ``layout="masked"`` (the decode variant): moe_dispatch_masked replaces
+        the permutation (fixed blocks of ``cap`` rows per local expert, default
+        T, so no slot is dropped) and the GEMMs run over those blocks
+        (grouped_gate_up_masked / grouped_down_masked); the combine reads the
+        slots' block rows."""
         dev = w_r.device
         self.T, self.d, self.f, self.k, self.eps = T, d, f, k, eps
         self.e_begin, self.e_count = e_begin, w_gate.shape[0]
@@ -458,6 +533,17 @@ class MoEFFNLayer:
         self.y_perm = torch.empty((rows, d), dtype=bf, device=dev)
         self.out = torch.empty((T, d), dtype=out_dtype, device=dev)
         self.act_fp8 = act_fp8
+        if layout not in ("contiguous", "masked"):
+            raise ValueError("MoEFFNLayer: layout is 'contiguous' or 'masked'")
+        self.layout = layout
+        if layout == "masked":
+            if act_fp8:
+                raise ValueError("MoEFFNLayer: the masked layout runs with bf16 activations")
+            self.cap = T if cap is None else cap
+            mrows = self.e_count * self.cap
+            self.row_index = torch.empty(mrows, dtype=torch.int32, device=dev)
+            self.h = torch.empty((mrows, f), dtype=bf, device=dev)
+            self.y_perm = torch.empty((mrows, d), dtype=bf, device=dev)
         if act_fp8:
             if w_gate.dtype != torch.float8_e4m3fn or s_gate is None:
                 raise ValueError("MoEFFNLayer: act_fp8 needs block-fp8 weights and scales")
@@ -481,6 +567,21 @@ class MoEFFNLayer:
         mark(1)
         moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, self.route_ws, stream=s)
         mark(2)
+        if self.layout == "masked":
+            moe_dispatch_masked(self.idx, self.e_begin, self.e_count, self.cap, counts=self.counts,
+                                row_index=self.row_index, pos=self.inv_pos,
+                                workspace=self.workspace, stream=s)
+            mark(3)
+            grouped_gate_up_masked(v, self.row_index, self.counts, self.cap, self.w[0], self.w[1],
+                                   self.s[0], self.s[1], h_out=self.h, stream=s)
+            mark(4)
+            grouped_down_masked(self.h, self.counts, self.cap, self.w[2], self.s[2],
+                                y_perm=self.y_perm, stream=s)
+            mark(5)
+            out = moe_combine(self.y_perm, self.inv_pos, self.topk_w, out=self.out,
+                              residual=residual, stream=s)
+            mark(6)
+            return out
         moe_permute(self.idx, self.e_begin, self.e_count, None, counts=self.counts,
                     offsets=self.offsets, src_token=self.src_token, inv_pos=self.inv_pos,
                     workspace=self.workspace, stream=s)

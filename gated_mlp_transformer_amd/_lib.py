@@ -39,6 +39,13 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
                            _c_void_p, _i32, _c_void_p]),
+    "moe_dispatch_masked": (_i32, [_c_void_p, _i64, _i32, _i32, _i32, _i32, _c_void_p,
+                                   _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "grouped_gate_up_masked": (_i32, [_c_void_p, _c_void_p, _i64, _c_void_p, _i32, _i32, _i32,
+                                      _i32, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p,
+                                      _c_void_p, _c_void_p]),
+    "grouped_down_masked": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _c_void_p,
+                                   _i32, _c_void_p, _c_void_p, _c_void_p]),
     "quantize_fp8_rows": (_i32, [_c_void_p, _i64, _c_void_p, _i32, _c_void_p, _c_void_p,
                                  _c_void_p]),
     "grouped_gate_up_a8": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i32, _i64,

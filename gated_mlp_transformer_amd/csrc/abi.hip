@@ -121,6 +121,22 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin, 
   return finish();
 }
 
+int moe_dispatch_masked(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
+                        int32_t e_count, int32_t cap, int32_t* counts, int32_t* row_index,
+                        int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!counts || !workspace) return MF_EINVAL;
+  if (T < 0 || k < 1 || e_begin < 0 || e_count < 1 || cap < 1) return MF_EINVAL;
+  if (T > 0 && (!topk_idx || !row_index || !pos)) return MF_EINVAL;  // NULL only if empty
+  if (k > 8 || e_count > 256 || T > kI32Max / 8 ||
+      static_cast<int64_t>(e_count) * cap > kI32Max)
+    return MF_EUNSUPPORTED;
+  if (workspace_bytes < mf::permute_workspace_bytes(T, e_count)) return MF_EINVAL;
+  if (!a16(workspace)) return MF_EUNSUPPORTED;
+  mf::launch_dispatch_masked(topk_idx, T, k, e_begin, e_count, cap, counts, row_index, pos,
+                             workspace, S(stream));
+  return finish();
+}
+
 namespace {
 
 // Shared validation of the grouped GEMM calls. Returns MF_OK when the launch
@@ -150,24 +166,25 @@ int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_
 void enqueue_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
                      const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
                      int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
-                     const float* s_gate, const float* s_up, void* h, hipStream_t s) {
+                     const float* s_gate, const float* s_up, void* h, hipStream_t s,
+                     const int32_t* counts = nullptr, int32_t cap = 0) {
   if (w_dtype == MF_BF16)
     mf::launch_gemm_gateup_bf16(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
-                                w_up, h, num_cus(), s);
+                                w_up, h, num_cus(), s, counts, cap);
   else
     mf::launch_gemm_gateup_fp8(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
-                               w_up, s_gate, s_up, h, num_cus(), s);
+                               w_up, s_gate, s_up, h, num_cus(), s, counts, cap);
 }
 
 void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_t max_rows,
                   int32_t f, int32_t d, const void* w_down, int32_t w_dtype, const float* s_down,
-                  void* y, hipStream_t s) {
+                  void* y, hipStream_t s, const int32_t* counts = nullptr, int32_t cap = 0) {
   if (w_dtype == MF_BF16)
     mf::launch_gemm_down_bf16(h, offsets, e_count, max_rows, f, d, w_down, y, false, num_cus(),
-                              s);
+                              s, counts, cap);
   else
     mf::launch_gemm_down_fp8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, num_cus(),
-                             s);
+                             s, counts, cap);
 }
 
 }  // namespace
@@ -276,6 +293,36 @@ int grouped_down_a8(const void* hq, const float* h_scale, const int32_t* offsets
   if (st != MF_OK || empty) return st;
   mf::launch_gemm_down_a8(hq, h_scale, offsets, e_count, max_rows, f, d, w_down, s_down, y_perm,
                           num_cus(), S(stream));
+  return finish();
+}
+
+int grouped_gate_up_masked(const void* x, const int32_t* row_index, int64_t src_rows,
+                           const int32_t* counts, int32_t cap, int32_t e_count, int32_t d,
+                           int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+                           const float* s_gate, const float* s_up, void* h_out, void* stream) {
+  if (!counts || cap < 1) return MF_EINVAL;
+  const int64_t max_rows = static_cast<int64_t>(e_count) * cap;
+  bool empty;
+  // check_grouped needs a non-NULL boundary table: the counts stand in for it
+  const int st = check_grouped(x, counts, e_count, max_rows, d, f, w_dtype, w_gate, w_up,
+                               s_gate, s_up, h_out, &empty, row_index, src_rows);
+  if (st != MF_OK || empty) return st;
+  enqueue_gate_up(x, row_index, src_rows, nullptr, e_count, max_rows, d, f, w_gate, w_up,
+                  w_dtype, s_gate, s_up, h_out, S(stream), counts, cap);
+  return finish();
+}
+
+int grouped_down_masked(const void* h, const int32_t* counts, int32_t cap, int32_t e_count,
+                        int32_t f, int32_t d, const void* w_down, int32_t w_dtype,
+                        const float* s_down, void* y_perm, void* stream) {
+  if (!counts || cap < 1) return MF_EINVAL;
+  const int64_t max_rows = static_cast<int64_t>(e_count) * cap;
+  bool empty;
+  const int st = check_grouped(h, counts, e_count, max_rows, d, f, w_dtype, w_down, w_down,
+                               s_down, s_down, y_perm, &empty);
+  if (st != MF_OK || empty) return st;
+  enqueue_down(h, nullptr, e_count, max_rows, f, d, w_down, w_dtype, s_down, y_perm, S(stream),
+               counts, cap);
   return finish();
 }
 

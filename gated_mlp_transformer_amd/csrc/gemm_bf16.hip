@@ -37,8 +37,9 @@
 // LDS buffer between the remaining MFMAs. Spreading the loads keeps the
 // address queue from stalling the MFMA issue.
 //
-// Schedule. Group boundaries come from the device-side offsets, so no host
-// sync is needed. Each workgroup computes the schedule itself: group e's
+// Schedule. Group boundaries come from the device-side offsets (or, in the
+// masked layout, from per-group counts within fixed blocks of cap rows), so
+// no host sync is needed. Each workgroup computes the schedule itself: group e's
 // ceil(rows_e / 32) sub-tiles are split into ceil(sub_e / MT) near-equal
 // chunks (so an expert's last chunk is not a sliver), a tile is one chunk
 // against one n-tile, and tiles are numbered group-major, then chunk, then
@@ -82,6 +83,8 @@ struct GemmParams {
   int ldc;                 // row stride of C (elements)
   int kc;                  // K range of one split: split y covers [y*kc, (y+1)*kc)
   int64_t c_split;         // elements between the C blocks of consecutive splits
+  const int32_t* counts;   // masked layout (offsets unused): group e owns rows
+  int cap;                 // [e*cap, e*cap + min(counts[e], cap)); nullptr: offsets
 };
 
 // A stage row is 64 bytes (four 16-byte chunks); chunk c of row r sits at
@@ -219,7 +222,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   int ntile = 0;
   if (tid < p.e_count) {
     int beg = 0, end = p.max_rows;
-    if (p.offsets != nullptr) {
+    if (p.counts != nullptr) {  // masked layout: fixed blocks of cap rows
+      beg = clampi(tid * p.cap, 0, p.max_rows);
+      end = clampi(beg + clampi(p.counts[tid], 0, p.cap), beg, p.max_rows);
+    } else if (p.offsets != nullptr) {
       beg = clampi(p.offsets[tid], 0, p.max_rows);
       end = clampi(p.offsets[tid + 1], beg, p.max_rows);
     }
@@ -397,24 +403,24 @@ int persistent_grid(int64_t max_rows, int bm, int e_count, bool dense, int nt, i
 void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src_rows,
                              const int32_t* offsets, int e_count, int64_t max_rows, int K, int N,
                              const void* w_gate, const void* w_up, void* h, int num_cus,
-                             hipStream_t s) {
+                             hipStream_t s, const int32_t* counts, int cap) {
   GemmParams p{static_cast<const char*>(a), a_rows, static_cast<int>(a_src_rows),
                static_cast<const char*>(w_gate),
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
-               static_cast<int>(max_rows), K, N / 32, N, N, K, 0};
-  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
-                                   N / 128, num_cus);
+               static_cast<int>(max_rows), K, N / 32, N, N, K, 0, counts, cap};
+  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
+                                   offsets == nullptr && counts == nullptr, N / 128, num_cus);
   gemm_bf16_kernel<MT_GROUPED, true, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                            int K, int N, const void* w_down, void* y, bool out_f32, int num_cus,
-                           hipStream_t s) {
+                           hipStream_t s, const int32_t* counts, int cap) {
   GemmParams p{static_cast<const char*>(a), nullptr, 0, static_cast<const char*>(w_down), nullptr,
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
-               N, N, K, 0};
-  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count, offsets == nullptr,
-                                   N / 256, num_cus);
+               N, N, K, 0, counts, cap};
+  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
+                                   offsets == nullptr && counts == nullptr, N / 256, num_cus);
   if (out_f32)
     gemm_bf16_kernel<MT_GROUPED, false, true><<<grid, 256, 0, s>>>(p);
   else

@@ -24,7 +24,9 @@
 // Experts with more than 16 rows are processed 16 rows at a time (the weights
 // are re-read per pass; decode shapes need one pass).
 //
-// Schedule. Items of experts without rows do not exist. The grid is persistent
+// Schedule. Items of experts without rows do not exist. An expert's rows are
+// [offsets[e], offsets[e+1]) of the contiguous layout, or in the masked
+// layout the first counts[e] rows of its fixed block [e*cap, (e+1)*cap). The grid is persistent
 // (one workgroup per CU) and workgroup b takes items b, b + G, b + 2G, ...:
 // with equal items, a few hundred of them over G workgroups leave the last
 // round nearly full, where one workgroup per item would leave a partial
@@ -55,6 +57,8 @@ struct Fp8Params {
   int e_count;
   int max_rows;
   int K, N;
+  const int32_t* counts;   // masked layout (offsets unused): expert e owns rows
+  int cap;                 // [e*cap, e*cap + min(counts[e], cap)); nullptr: offsets
 };
 
 template <int R>
@@ -78,8 +82,14 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
   // ---- device-side item list: prefix over experts of ntw items per active expert
   int items = 0;
   if (tid < p.e_count) {
-    const int beg = clampi(p.offsets[tid], 0, p.max_rows);
-    const int end = clampi(p.offsets[tid + 1], beg, p.max_rows);
+    int beg, end;
+    if (p.counts != nullptr) {  // masked layout: fixed blocks of cap rows
+      beg = clampi(tid * p.cap, 0, p.max_rows);
+      end = clampi(beg + clampi(p.counts[tid], 0, p.cap), beg, p.max_rows);
+    } else {
+      beg = clampi(p.offsets[tid], 0, p.max_rows);
+      end = clampi(p.offsets[tid + 1], beg, p.max_rows);
+    }
     s_beg[tid] = beg;
     s_end[tid] = end;
     items = end > beg ? ntw : 0;
@@ -210,19 +220,21 @@ unsigned fp8_grid(int e_count, int N, int ntw, int num_cus) {
 void launch_gemm_gateup_fp8(const void* a, const int32_t* a_rows, int64_t a_src_rows,
                             const int32_t* offsets, int e_count, int64_t max_rows, int K, int N,
                             const void* w_gate, const void* w_up, const float* s_gate,
-                            const float* s_up, void* h, int num_cus, hipStream_t s) {
+                            const float* s_up, void* h, int num_cus, hipStream_t s,
+                            const int32_t* counts, int cap) {
   Fp8Params p{static_cast<const char*>(a), a_rows, static_cast<int>(a_src_rows),
               static_cast<const uint8_t*>(w_gate),
               static_cast<const uint8_t*>(w_up), s_gate, s_up, static_cast<char*>(h), offsets,
-              e_count, static_cast<int>(max_rows), K, N};
+              e_count, static_cast<int>(max_rows), K, N, counts, cap};
   gemm_fp8_kernel<true><<<dim3(fp8_grid(e_count, N, 256, num_cus)), 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
                           int K, int N, const void* w_down, const float* s_down, void* y,
-                          int num_cus, hipStream_t s) {
+                          int num_cus, hipStream_t s, const int32_t* counts, int cap) {
   Fp8Params p{static_cast<const char*>(a), nullptr, 0, static_cast<const uint8_t*>(w_down), nullptr, s_down,
-              nullptr, static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N};
+              nullptr, static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N,
+              counts, cap};
   gemm_fp8_kernel<false><<<dim3(fp8_grid(e_count, N, 512, num_cus)), 256, 0, s>>>(p);
 }
 

@@ -23,6 +23,12 @@ void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_cou
                     int32_t* offsets, int32_t* src_token, int32_t* inv_pos,
                     void* workspace, hipStream_t s);
 
+// Masked (fixed-capacity) dispatch: counts [e_count], row_index [e_count*cap],
+// pos [T,k] (row e*cap + rank, or -1); workspace as launch_permute's.
+void launch_dispatch_masked(const int32_t* idx, int64_t T, int k, int e_begin, int e_count,
+                            int cap, int32_t* counts, int32_t* row_index, int32_t* pos,
+                            void* workspace, hipStream_t s);
+
 // Weight packing into MFMA fragment order (pack.hip).
 size_t packed_bytes(int64_t groups, int N, int K, bool fp8);
 void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8,
@@ -34,10 +40,11 @@ void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool 
 void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src_rows,
                              const int32_t* offsets, int e_count, int64_t max_rows, int K,
                              int N, const void* w_gate, const void* w_up, void* h, int num_cus,
-                             hipStream_t s);
+                             hipStream_t s, const int32_t* counts = nullptr, int cap = 0);
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count,
                            int64_t max_rows, int K, int N, const void* w_down,
-                           void* y, bool out_f32, int num_cus, hipStream_t s);
+                           void* y, bool out_f32, int num_cus, hipStream_t s,
+                           const int32_t* counts = nullptr, int cap = 0);
 
 // C_y = A[:, y*K/splits : (y+1)*K/splits] B[:n_valid, same]^T in fp32 for each K
 // split y (one group, bf16 operands). Requires (K / splits) % 256 == 0.
@@ -48,10 +55,12 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
 void launch_gemm_gateup_fp8(const void* a, const int32_t* a_rows, int64_t a_src_rows,
                             const int32_t* offsets, int e_count, int64_t max_rows, int K,
                             int N, const void* w_gate, const void* w_up, const float* s_gate,
-                            const float* s_up, void* h, int num_cus, hipStream_t s);
+                            const float* s_up, void* h, int num_cus, hipStream_t s,
+                            const int32_t* counts = nullptr, int cap = 0);
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
                           int64_t max_rows, int K, int N, const void* w_down,
-                          const float* s_down, void* y, int num_cus, hipStream_t s);
+                          const float* s_down, void* y, int num_cus, hipStream_t s,
+                          const int32_t* counts = nullptr, int cap = 0);
 
 // fp8 activations ([rows, K] codes + [rows, K/128] f32 group scales) against
 // block-fp8 weights on the fp8 MFMA; bf16 out (gate/up: SiLU(g) * u).

@@ -193,6 +193,87 @@ __global__ __launch_bounds__(256) void permute_place_kernel(
   }
 }
 
+// Masked layout (the decode variant: fixed per-expert capacity, no prefix
+// over experts). Local expert e owns rows [e*cap, (e+1)*cap); slot (t, j)
+// routed to e goes to row e*cap + rank, rank = the number of earlier tokens
+// routed to e (earlier blocks' counts + popcounts of the block's wave masks,
+// as in the contiguous placement); a slot whose rank reaches cap is dropped
+// (pos -1). counts[e] = min(total, cap). With one block of tokens the totals
+// come from the block's own masks and the count pass is skipped.
+template <bool ONE_BLOCK>
+__global__ __launch_bounds__(256) void dispatch_masked_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int k, int e_begin, int e_count, int cap,
+    int64_t B, const int32_t* __restrict__ cnt, int32_t* __restrict__ counts,
+    int32_t* __restrict__ row_index, int32_t* __restrict__ pos) {
+  __shared__ unsigned long long m[kWaves][kMaxLocal];
+  __shared__ int rank0[kMaxLocal];  // earlier blocks' slots, per expert
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int64_t b = blockIdx.x;
+  for (int i = tid; i < kWaves * kMaxLocal; i += 256) (&m[0][0])[i] = 0ull;
+  __syncthreads();
+  const int64_t t = b * kBlockTok + tid;
+  int ex[8];  // k <= 8; slots past k stay -1 (not local)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ex[j] = -1;
+    if (t < T && j < k) {
+      ex[j] = idx[t * k + j] - e_begin;
+      if (ex[j] >= 0 && ex[j] < e_count) atomicOr(&m[wave][ex[j]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (tid < e_count) {
+    int before = 0, total = 0;
+    if constexpr (ONE_BLOCK) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) total += __popcll(m[w][tid]);
+    } else {
+      for (int64_t q = 0; q < B; ++q) {
+        const int c = cnt[q * e_count + tid];
+        before += q < b ? c : 0;
+        total += c;
+      }
+    }
+    rank0[tid] = before;
+    if (b == 0) counts[tid] = min(total, cap);
+  }
+  __syncthreads();
+  if (t >= T) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const int e = ex[j];
+    int p = -1;
+    if (e >= 0 && e < e_count) {
+      int r = rank0[e] + __popcll(m[wave][e] & below);
+      for (int w = 0; w < wave; ++w) r += __popcll(m[w][e]);
+      if (r < cap) {
+        p = e * cap + r;
+        row_index[p] = static_cast<int32_t>(t);
+      }
+    }
+    pos[t * k + j] = p;
+  }
+}
+
+void launch_dispatch_masked(const int32_t* idx, int64_t T, int k, int e_begin, int e_count,
+                            int cap, int32_t* counts, int32_t* row_index, int32_t* pos,
+                            void* workspace, hipStream_t s) {
+  const int64_t B = (T + kBlockTok - 1) / kBlockTok;
+  if (B <= 1) {  // also T == 0: one block writes zero counts
+    dispatch_masked_kernel<true><<<1, 256, 0, s>>>(idx, T, k, e_begin, e_count, cap, 1, nullptr,
+                                                   counts, row_index, pos);
+    return;
+  }
+  Workspace ws = carve(workspace, B, e_count);
+  const dim3 grid(static_cast<unsigned>(B));
+  permute_count_kernel<<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, ws);
+  dispatch_masked_kernel<false><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, cap, B, ws.cnt,
+                                                     counts, row_index, pos);
+}
+
 // x_perm[r] = x[src_token[r]] for r < min(offsets[e_count], max_rows).
 __global__ __launch_bounds__(256) void permute_gather_kernel(
     const char* __restrict__ x, int64_t T, int64_t row_bytes, const int32_t* __restrict__ src_token,

@@ -166,6 +166,31 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * moe_dispatch_masked - the masked (fixed-capacity) layout of the routing
+ * slots, the decode variant of the permutation ("「赤兔」Chitu 框架深度解读（七）：MoE":
+ * the decode experts run as a masked GEMM (deepgemm_masked), the decode
+ * dispatcher is the low-latency one). Local expert e owns rows
+ * [e*cap, (e+1)*cap); slot (t, j) routed to a local expert e goes to row
+ * e*cap + rank, rank = the number of earlier tokens routed to e (stable, token
+ * order). There is no prefix over experts. A slot whose rank reaches cap is
+ * dropped (pos = -1, it adds nothing in moe_combine); with cap >= T nothing is
+ * dropped (a token picks an expert at most once).
+ *
+ * topk_idx  [T, k] int32 (moe_route's ids); T >= 0, 1 <= k <= 8
+ * e_begin, e_count  local experts [e_begin, e_begin + e_count), e_count <= 256
+ * cap       rows per expert block, >= 1 (e_count * cap < 2^31)
+ * counts    [e_count] int32 out: rows used in each block, min(routed, cap)
+ * row_index [e_count * cap] int32 out: token of each used row (rows past
+ *           counts[e] are not written); the masked GEMMs gather V[row_index]
+ * pos       [T, k] int32 out: row of each slot, or -1
+ * workspace moe_permute_workspace_size(T, k, e_count) bytes (16-byte aligned)
+ * Deterministic and bit-exact (no order-dependent atomics).
+ */
+int moe_dispatch_masked(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
+                        int32_t e_count, int32_t cap, int32_t* counts, int32_t* row_index,
+                        int32_t* pos, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * grouped_swiglu - every local expert's gated MLP over its contiguous rows:
  *   H[o_e:o_{e+1}]      = SiLU(X_perm W_gate_e) * (X_perm W_up_e)
  *   Y_perm[o_e:o_{e+1}] = H[o_e:o_{e+1}] W_down_e
@@ -225,6 +250,25 @@ int grouped_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
 int grouped_down(const void* h, const int32_t* offsets, int32_t e_count,
                  int64_t max_rows, int32_t f, int32_t d, const void* w_down,
                  int32_t w_dtype, const float* s_down, void* y_perm, void* stream);
+
+/*
+ * grouped_gate_up_masked / grouped_down_masked - grouped_gate_up /
+ * grouped_down over the masked layout (moe_dispatch_masked): expert e's rows
+ * are the first counts[e] (clamped to cap) rows of its block [e*cap, (e+1)*cap).
+ * The passages, weights, dtypes and requirements are grouped_swiglu's, with
+ * max_rows = e_count * cap:
+ *   x, row_index, src_rows as grouped_swiglu (row_index = moe_dispatch_masked's)
+ *   h_out / h  [e_count*cap, f] bf16, y_perm [e_count*cap, d] bf16; rows past
+ *   counts[e] in each block are not written. moe_combine takes pos as inv_pos
+ *   with max_rows = e_count * cap.
+ */
+int grouped_gate_up_masked(const void* x, const int32_t* row_index, int64_t src_rows,
+                           const int32_t* counts, int32_t cap, int32_t e_count, int32_t d,
+                           int32_t f, const void* w_gate, const void* w_up, int32_t w_dtype,
+                           const float* s_gate, const float* s_up, void* h_out, void* stream);
+int grouped_down_masked(const void* h, const int32_t* counts, int32_t cap, int32_t e_count,
+                        int32_t f, int32_t d, const void* w_down, int32_t w_dtype,
+                        const float* s_down, void* y_perm, void* stream);
 
 /*
  * quantize_fp8_rows - per-token fp8 activations for the block-fp8 prefill

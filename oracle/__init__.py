@@ -48,6 +48,7 @@ from .ffn import (  # noqa: F401
     route,
     route_weights,
     permute,
+    dispatch_masked,
     experts,
     combine,
     moe_ffn,

@@ -286,6 +286,34 @@ def permute(idx, e_begin: int, e_count: int, x=None):
     return counts, offsets, src_token, inv_pos.astype(np.int64), x_perm
 
 
+def dispatch_masked(idx, e_begin: int, e_count: int, cap: int):
+    """Masked (fixed-capacity) layout of the routing slots ([P5] decode: masked
+    expert GEMM; READING R34).
+
+    Local expert e owns rows ``[e*cap, (e+1)*cap)``. Walking the slots in
+    token order, slot (t, j) of a local expert e gets rank = the number of
+    earlier tokens routed to e; it goes to row ``e*cap + rank`` if rank < cap,
+    else it is dropped (-1). Returns ``(counts [e_count] = min(routed, cap),
+    row_token [e_count*cap] (-1 where unused), pos [T,k])``.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    seen = [0] * e_count
+    row_token = np.full(e_count * cap, -1, dtype=np.int64)
+    pos = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j]) - e_begin
+            if 0 <= e < e_count:
+                r = seen[e]
+                seen[e] += 1
+                if r < cap:
+                    pos[t, j] = e * cap + r
+                    row_token[e * cap + r] = t
+    counts = np.minimum(np.array(seen, dtype=np.int64), cap)
+    return counts, row_token, pos
+
+
 # ---------------------------------------------------------------------------
 # experts  ([P1] EP 路径: grouped GEMM; [P5] BatchedExperts)
 # ---------------------------------------------------------------------------

@@ -185,3 +185,34 @@ def test_fp8_prefill_validation(lib):
     assert dn(y=N) == MF_EINVAL
     assert dn(f=640) == MF_EUNSUPPORTED
     assert dn(rows=0, hq=N, hs=N, y=N) == MF_OK
+
+
+def test_masked_layout_validation(lib):
+    ws = lib.moe_permute_workspace_size(64, 8, 16)
+
+    def disp(**kw):
+        a = dict(idx=P, T=64, k=8, eb=0, ec=16, cap=64, cnt=P, ri=P, pos=P, wsp=P, wsb=ws)
+        a.update(kw)
+        return lib.moe_dispatch_masked(a["idx"], a["T"], a["k"], a["eb"], a["ec"], a["cap"],
+                                       a["cnt"], a["ri"], a["pos"], a["wsp"], a["wsb"], N)
+    assert disp(cnt=N) == MF_EINVAL
+    assert disp(cap=0) == MF_EINVAL
+    assert disp(ri=N) == MF_EINVAL
+    assert disp(wsb=0) == MF_EINVAL
+    assert disp(k=9) == MF_EUNSUPPORTED
+    assert disp(ec=257) == MF_EUNSUPPORTED
+    assert disp(ec=256, cap=1 << 24) == MF_EUNSUPPORTED   # e_count * cap >= 2^31
+
+    def gu(**kw):
+        a = dict(x=P, ri=P, src=64, cnt=P, cap=64, ec=4, d=256, f=256, wg=P, wu=P, wdt=BF16,
+                 sg=N, su=N, h=P)
+        a.update(kw)
+        return lib.grouped_gate_up_masked(a["x"], a["ri"], a["src"], a["cnt"], a["cap"], a["ec"],
+                                          a["d"], a["f"], a["wg"], a["wu"], a["wdt"], a["sg"],
+                                          a["su"], a["h"], N)
+    assert gu(cnt=N) == MF_EINVAL
+    assert gu(cap=0) == MF_EINVAL
+    assert gu(wdt=FP8) == MF_EINVAL        # fp8 weights need their scales
+    assert gu(d=384) == MF_EUNSUPPORTED
+    assert lib.grouped_down_masked(P, N, 64, 4, 256, 256, P, BF16, N, P, N) == MF_EINVAL
+    assert lib.grouped_down_masked(P, P, 64, 4, 256, 320, P, BF16, N, P, N) == MF_EUNSUPPORTED

@@ -280,3 +280,45 @@ def test_workload_prefill_8192tok_fp8_activations(g):
                       spec["e_count"], "fp8", token_sample=tokens,
                       col_sample=list(range(128, 160)) + [2047], e2e_tokens=tokens[:6])
     assert res["S"] == to_i64(layer.counts).sum()
+
+
+def _masked_twin(g, inp, T, d, f, eb, cap=None):
+    return g.MoEFFNLayer(T=T, d=d, f=f, w_r=inp["w_r"], bias=inp["bias"], gamma=inp.get("gamma"),
+                         w_gate=inp["w_gate"], w_up=inp["w_up"], w_down=inp["w_down"],
+                         e_begin=eb, s_gate=inp.get("s_gate"), s_up=inp.get("s_up"),
+                         s_down=inp.get("s_down"), layout="masked", cap=cap)
+
+
+@pytest.mark.parametrize("wdtype,T,eb,ec", [("bf16", 200, 16, 16), ("fp8", 64, 0, 64)])
+def test_masked_layout_equals_contiguous(g, wdtype, T, eb, ec):
+    """The masked (fixed-capacity) layout changes where rows live, not their
+    arithmetic: the layer output is bit-identical to the contiguous layer's,
+    which check_layer ties to the oracle; the dispatch integers are the
+    oracle's."""
+    d, f, E = 256, 256, 64
+    inp = make_moe(T, d, f, E, eb, ec, wdtype=wdtype, seed=T + ec + 9, device=DEV)
+    contig = build_layer(g, inp, T, d, f, eb)
+    check_layer(g, contig, inp, T, d, f, E, eb, ec, wdtype)
+    masked = _masked_twin(g, inp, T, d, f, eb)
+    a = contig(inp["x"]).clone()
+    b = masked(inp["x"]).clone()
+    torch.cuda.synchronize()
+    counts, rows, pos = oracle.dispatch_masked(to_i64(masked.idx), eb, ec, T)
+    assert np.array_equal(to_i64(masked.counts), counts)
+    assert np.array_equal(to_i64(masked.inv_pos), pos)
+    used = rows >= 0
+    assert np.array_equal(to_i64(masked.row_index)[used], rows[used])
+    assert torch.equal(a, b)
+
+
+def test_workload_decode_64tok_fp8_masked(g):
+    spec = WORKLOADS["moe_decode_64tok_256exp_fp8"]
+    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
+                   wdtype="fp8", device=DEV)
+    contig = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    masked = _masked_twin(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    a = contig(inp["x"]).clone()
+    b = masked(inp["x"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert int(masked.counts.sum()) == spec["T"] * 8

@@ -157,6 +157,80 @@ def test_permute_zero_tokens_writes_zero_counts(g):
     assert res.offsets.cpu().tolist() == [0] * 17
 
 
+@pytest.mark.parametrize("T,E,k,eb,ec,cap", [
+    (64, 256, 8, 0, 256, 64),     # decode shape, one block, nothing dropped
+    (0, 32, 8, 0, 16, 4),         # no tokens: zero counts
+    (255, 64, 8, 3, 40, 255),
+    (1000, 64, 8, 0, 64, 1000),   # several blocks
+    (1000, 64, 6, 5, 30, 40),     # capacity drops, k below 8
+    (300, 16, 8, 0, 16, 7),
+])
+def test_dispatch_masked(g, T, E, k, eb, ec, cap):
+    idx = routing_ids(T, E, k, seed=T * 3 + cap) if T else torch.zeros((0, k), dtype=torch.int32, device=DEV)
+    row_index = torch.full((ec * cap,), -7, dtype=torch.int32, device=DEV)
+    res = g.moe_dispatch_masked(idx, eb, ec, cap, row_index=row_index)
+    torch.cuda.synchronize()
+    counts, rows, pos = oracle.dispatch_masked(to_i64(idx) if T else np.zeros((0, k)), eb, ec, cap)
+    assert np.array_equal(to_i64(res.counts), counts)
+    got_rows = to_i64(res.row_index)
+    used = rows >= 0
+    assert np.array_equal(got_rows[used], rows[used])
+    assert (got_rows[~used] == -7).all()          # unused rows are not written
+    if T:
+        assert np.array_equal(to_i64(res.pos), pos)
+
+
+@pytest.mark.parametrize("wdtype,counts,cap,d,f", [
+    ("bf16", [0, 1, 130, 257, 3], 300, 256, 768),
+    ("bf16", [1, 33, 65, 97], 128, 256, 256),
+    ("fp8", [1, 3, 0, 17, 2, 16], 20, 256, 512),
+    ("fp8", [64] * 4, 64, 512, 256),
+])
+def test_grouped_masked_matches_contiguous(g, wdtype, counts, cap, d, f):
+    """The masked GEMMs over blocks of cap rows give, row for row, the
+    contiguous GEMMs' results (same per-row arithmetic) and match the oracle."""
+    ec = len(counts)
+    S = int(sum(counts))
+    W = _expert_weights(ec, d, f, wdtype, seed=S + cap)
+    pw = [g.pack_weights(W[k_]) for k_ in ("w_gate", "w_up", "w_down")]
+    src_rows = max(1, S // 2 + 5)
+    x_src = synth.normal((src_rows, d), name="t.gm.x", sub=S, device=DEV)
+    tok = synth.integers((S,), 0, src_rows, name="t.gm.tok", sub=S).to(torch.int32).to(DEV)
+    # contiguous: rows grouped by expert; masked: the same rows at e*cap + r
+    offsets = _offsets(counts)
+    row_index = torch.full((ec * cap,), 0, dtype=torch.int32, device=DEV)
+    off = offsets.cpu().numpy()
+    for e in range(ec):
+        row_index[e * cap:e * cap + counts[e]] = tok[off[e]:off[e + 1]]
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    h_c = torch.empty((S + 1, f), dtype=torch.bfloat16, device=DEV)
+    y_c = torch.empty((S + 1, d), dtype=torch.bfloat16, device=DEV)
+    tok_pad = torch.cat([tok, tok[:1]])
+    g.grouped_gate_up(x_src, offsets, pw[0], pw[1], W.get("s_gate"), W.get("s_up"),
+                      row_index=tok_pad, h_out=h_c)
+    g.grouped_down(h_c, offsets, pw[2], W.get("s_down"), y_perm=y_c)
+    h_m = torch.full((ec * cap, f), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y_m = torch.full((ec * cap, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    g.grouped_gate_up_masked(x_src, row_index, cnt, cap, pw[0], pw[1], W.get("s_gate"),
+                             W.get("s_up"), h_out=h_m)
+    g.grouped_down_masked(h_m, cnt, cap, pw[2], W.get("s_down"), y_perm=y_m)
+    torch.cuda.synchronize()
+    xs = to_f64(x_src)
+    for e in range(ec):
+        a, b = off[e], off[e + 1]
+        blk = slice(e * cap, e * cap + counts[e])
+        assert torch.equal(h_m[blk], h_c[a:b]) and torch.equal(y_m[blk], y_c[a:b])
+        # rows past the count in each block are not written
+        assert torch.isnan(h_m[e * cap + counts[e]:(e + 1) * cap].float()).all()
+        if b > a:
+            wg, wu, wd = _oracle_weights(W, e, wdtype)
+            xe = xs[to_i64(tok[a:b])]
+            rel = 5e-3 if wdtype == "bf16" else REL_FP8
+            assert_fp("H masked", to_f64(h_m[blk]), oracle.silu(xe @ wg) * (xe @ wu), rel=rel,
+                      max_abs=None)
+            assert_fp("Y masked", to_f64(y_m[blk]), to_f64(h_m[blk]) @ wd, rel=rel, max_abs=None)
+
+
 # ------------------------------------------------------------------ packing --
 
 def _pack_reference(w: np.ndarray, fp8: bool) -> np.ndarray:

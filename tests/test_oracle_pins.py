@@ -379,3 +379,55 @@ def test_moe_ffn_matches_per_token_definition():
                 h = F.silu(torch.from_numpy(v[t] @ wg)).numpy() * (v[t] @ wu)
                 acc += s[e] / s[top].sum() * (h @ wd)
         assert np.allclose(res["out"][t], acc, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------- masked dispatch --
+
+def test_dispatch_masked_blocks_are_the_contiguous_buckets():
+    r = rng(21)
+    T, E, k, eb, ec = 50, 24, 8, 4, 12
+    idx = np.sort(np.stack([r.choice(E, k, replace=False) for _ in range(T)]), axis=1)
+    counts, offsets, src, inv, _ = oracle.permute(idx, eb, ec)
+    cap = T  # a token picks an expert at most once: nothing is dropped
+    mc, rows, pos = oracle.dispatch_masked(idx, eb, ec, cap)
+    assert np.array_equal(mc, counts)
+    for e in range(ec):
+        blk = rows[e * cap:(e + 1) * cap]
+        assert np.array_equal(blk[:counts[e]], src[offsets[e]:offsets[e + 1]])
+        assert (blk[counts[e]:] == -1).all()
+    local = inv >= 0
+    e_of = idx - eb
+    assert np.array_equal(pos >= 0, local)
+    assert np.array_equal(pos[local] - e_of[local] * cap,
+                          inv[local] - offsets[e_of[local]])
+
+
+def test_dispatch_masked_capacity_keeps_the_first_tokens():
+    r = rng(22)
+    T, E, k, cap = 40, 10, 4, 3
+    idx = np.sort(np.stack([r.choice(E, k, replace=False) for _ in range(T)]), axis=1)
+    mc, rows, pos = oracle.dispatch_masked(idx, 0, E, cap)
+    for e in range(E):
+        toks = np.nonzero((idx == e).any(axis=1))[0]      # ascending token ids routed to e
+        keep = toks[:cap]
+        assert mc[e] == len(keep)
+        assert np.array_equal(rows[e * cap:e * cap + len(keep)], keep)
+        for t in toks[cap:]:                               # dropped slots
+            assert pos[t][idx[t] == e][0] == -1
+
+
+def test_combine_is_layout_independent():
+    r = rng(23)
+    T, E, k, d = 30, 16, 8, 5
+    idx = np.sort(np.stack([r.choice(E, k, replace=False) for _ in range(T)]), axis=1)
+    w = r.uniform(0, 1, (T, k))
+    val = r.normal(0, 1, (T, k, d))                       # the expert output of each slot
+    counts, offsets, src, inv, _ = oracle.permute(idx, 0, E)
+    y_c = np.zeros((T * k, d))
+    mc, rows, pos = oracle.dispatch_masked(idx, 0, E, T)
+    y_m = np.zeros((E * T, d))
+    for t in range(T):
+        for j in range(k):
+            y_c[inv[t, j]] = val[t, j]
+            y_m[pos[t, j]] = val[t, j]
+    assert np.allclose(oracle.combine(y_c, inv, w), oracle.combine(y_m, pos, w), rtol=0, atol=0)
