@@ -36,6 +36,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PREFILL = "moe_prefill_8192tok_32exp_bf16"
 DECODE = "moe_decode_64tok_256exp_fp8"
 PREFILL_FP8 = "moe_prefill_8192tok_32exp_fp8act"
+DECODE_MASKED = "moe_decode_64tok_256exp_fp8_masked"
 DENSE = "norm_tp_shard_bf16_4096"
 ROUTER = "router_4096tok_E256"
 
@@ -51,9 +52,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the decode / fp8-activation prefill / dense-shard / router-only "
+                    help="skip the decode (contiguous and masked) / fp8-activation prefill / "
+                         "dense-shard / router-only "
                          "measurements")
-    ap.add_argument("--only", choices=["prefill", "decode", "dense", "router", "prefill_fp8"],
+    ap.add_argument("--only", choices=["prefill", "decode", "dense", "router", "prefill_fp8",
+                                       "decode_masked"],
                     default=None,
                     help="run one workload only (for profiling); prints its stage times")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -168,7 +171,8 @@ def build_layer(spec, device, seed=0):
                           bias=inp["bias"], gamma=inp["gamma"], w_gate=inp["w_gate"],
                           w_up=inp["w_up"], w_down=inp["w_down"], e_begin=spec["e_begin"],
                           s_gate=inp.get("s_gate"), s_up=inp.get("s_up"),
-                          s_down=inp.get("s_down"), act_fp8=spec.get("act_fp8", False))
+                          s_down=inp.get("s_down"), act_fp8=spec.get("act_fp8", False),
+                          layout=spec.get("layout", "contiguous"))
     return layer, inp
 
 
@@ -179,7 +183,7 @@ def run_moe(name, steps, warmup):
     log(f"[bench] {name}: building inputs")
     layer, inp = build_layer(spec, "cuda")
     ms, us, wall = time_layer(layer, inp["x"], steps, warmup)
-    S = int(layer.offsets[-1].item())
+    S = int(layer.counts.sum().item())  # both layouts (offsets are unused when masked)
     active = int((layer.counts > 0).sum().item())
     counts = layer.counts.cpu()
     welt = 2 if spec["wdtype"] == "bf16" else 1
@@ -347,8 +351,9 @@ def main():
             torch.cuda.synchronize()
             del src, dst
             log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
-        if args.only in ("prefill", "decode", "prefill_fp8"):
-            name = {"prefill": PREFILL, "decode": DECODE, "prefill_fp8": PREFILL_FP8}[args.only]
+        if args.only in ("prefill", "decode", "prefill_fp8", "decode_masked"):
+            name = {"prefill": PREFILL, "decode": DECODE, "prefill_fp8": PREFILL_FP8,
+                    "decode_masked": DECODE_MASKED}[args.only]
             res = run_moe(name, args.steps, args.warmup)
             peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
@@ -410,6 +415,14 @@ def main():
                               gemm_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                           "stages": dstage}
         del dec
+        torch.cuda.empty_cache()
+        dm = run_moe(DECODE_MASKED, max(10, args.steps // 2), args.warmup)
+        line["decode_masked"] = {
+            "workload": DECODE_MASKED, "tokens_per_s": round(64 / (dm["ms"] * 1e-3), 1),
+            "ms_per_step": round(dm["ms"], 4),
+            "vs_contiguous_step": round(line["decode"]["ms_per_step"] / dm["ms"], 4),
+            "stages": stage_report(dm["work"], dm["us"])}
+        del dm
         torch.cuda.empty_cache()
         p8 = run_moe(PREFILL_FP8, max(10, args.steps // 2), args.warmup)
         gw = p8["work"]["grouped_gate_up"]["flops"] + p8["work"]["grouped_down"]["flops"]

@@ -16,6 +16,8 @@ the builder functions also take smaller shapes for parity cases.
   moe_prefill_8192tok_32exp_fp8act the prefill shape and routing with the experts
                                    drawn ~N(0,0.02) f32 then block-fp8 quantised,
                                    run with fp8 activations (per-token 1x128)
+  moe_decode_64tok_256exp_fp8_masked  the decode workload in the masked layout
+                                   (fixed blocks of 64 rows per expert)
   moe_decode_64tok_256exp_fp8      64 tokens, all 256 experts local, experts
                                    drawn ~N(0,0.02) f32 then block-fp8 quantised
 """
@@ -45,6 +47,9 @@ WORKLOADS = {
     "moe_decode_64tok_256exp_fp8": dict(kind="moe", T=64, d=4096, f=2048, E=256,
                                         e_begin=0, e_count=256, wdtype="fp8",
                                         zipf=0.0),
+    "moe_decode_64tok_256exp_fp8_masked": dict(kind="moe", T=64, d=4096, f=2048, E=256,
+                                               e_begin=0, e_count=256, wdtype="fp8",
+                                               zipf=0.0, layout="masked"),
 }
 
 
