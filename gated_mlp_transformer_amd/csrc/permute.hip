@@ -118,7 +118,9 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int64_t B, int e_coun
   if (e == 0) offsets[0] = 0;
 }
 
-template <bool SELF_SCAN>
+// With a single block of tokens (decode) the totals are the block's own
+// bitmap popcounts, so the count pass is skipped (ONE_BLOCK: one launch).
+template <bool SELF_SCAN, bool ONE_BLOCK = false>
 __global__ __launch_bounds__(256) void permute_place_kernel(
     const int32_t* __restrict__ idx, int64_t T, int k, int e_begin, int e_count, int64_t B,
     Workspace ws, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -130,7 +132,34 @@ __global__ __launch_bounds__(256) void permute_place_kernel(
   const int wave = tid / kWave, lane = tid % kWave;
   const int64_t b = blockIdx.x;
   for (int i = tid; i < kWaves * kMaxLocal; i += 256) (&m[0][0])[i] = 0ull;
-  if constexpr (SELF_SCAN) {
+  const int64_t t = b * kBlockTok + tid;
+  int ex[8];  // k <= 8; slots past k stay -1 (not local)
+  if constexpr (ONE_BLOCK) {  // bitmaps first: they give the totals
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ex[j] = -1;
+      if (t < T && j < k) {
+        ex[j] = idx[t * k + j] - e_begin;
+        if (ex[j] >= 0 && ex[j] < e_count) atomicOr(&m[wave][ex[j]], 1ull << lane);
+      }
+    }
+    __syncthreads();
+    int total = 0;
+    if (tid < e_count) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) total += __popcll(m[w][tid]);
+    }
+    sc[tid] = tid < e_count ? total : 0;
+    __syncthreads();
+    block_inclusive_scan(sc);
+    if (tid < e_count) {
+      row0[tid] = sc[tid] - total;
+      counts[tid] = total;
+      offsets[tid + 1] = sc[tid];
+    }
+    if (tid == 0) offsets[0] = 0;
+  } else if constexpr (SELF_SCAN) {
     // per expert (thread e): earlier blocks' slots and the total
     int before = 0, total = 0;
     if (tid < e_count) {
@@ -166,17 +195,17 @@ __global__ __launch_bounds__(256) void permute_place_kernel(
     if (tid < e_count) row0[tid] = offsets[tid] + ws.base[b * e_count + tid];
   }
   __syncthreads();
-  const int64_t t = b * kBlockTok + tid;
-  int ex[8];  // k <= 8; slots past k stay -1 (not local)
+  if constexpr (!ONE_BLOCK) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    ex[j] = -1;
-    if (t < T && j < k) {
-      ex[j] = idx[t * k + j] - e_begin;
-      if (ex[j] >= 0 && ex[j] < e_count) atomicOr(&m[wave][ex[j]], 1ull << lane);
+    for (int j = 0; j < 8; ++j) {
+      ex[j] = -1;
+      if (t < T && j < k) {
+        ex[j] = idx[t * k + j] - e_begin;
+        if (ex[j] >= 0 && ex[j] < e_count) atomicOr(&m[wave][ex[j]], 1ull << lane);
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   if (t >= T) return;
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
@@ -313,13 +342,16 @@ void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_cou
   const int64_t B = (T + kBlockTok - 1) / kBlockTok;
   Workspace ws = carve(workspace, B, e_count);
   const dim3 grid(static_cast<unsigned>(B));
-  if (B > 0)
+  if (B == 1) {  // one token block: a single launch
+    permute_place_kernel<true, true><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, B, ws,
+                                                          counts, offsets, src_token, inv_pos);
+  } else if (B > 0 && B * e_count <= kSelfScanMax) {
     permute_count_kernel<<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, ws);
-  if (B > 0 && B * e_count <= kSelfScanMax) {
     permute_place_kernel<true><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, B, ws, counts,
                                                     offsets, src_token, inv_pos);
   } else {
     // also for T == 0: zero counts and offsets
+    if (B > 0) permute_count_kernel<<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, ws);
     permute_scan_kernel<<<1, 256, 0, s>>>(B, e_count, ws, counts, offsets);
     if (B > 0)
       permute_place_kernel<false><<<grid, 256, 0, s>>>(idx, T, k, e_begin, e_count, B, ws,
