@@ -30,8 +30,8 @@
 // straight from global memory into registers three stages ahead (a ring of
 // four slots); the activation and weight scales of the next stage are loaded
 // with it. The fp8 weights use the same packed order as the decode kernels
-// (16-row x 128-column blocks, pack.hip); a lane gathers its 32 bytes of a
-// 32-row fragment from the two 16-row blocks.
+// (16-row x 128-column blocks, slab-major, pack.hip); a lane gathers its 32
+// bytes of a 32-row fragment from the two 16-row blocks.
 //
 // Schedule. As the bf16 grouped GEMM: each expert's rows split into
 // near-equal chunks of at most MT 32-row sub-tiles, tiles numbered expert /
@@ -94,8 +94,8 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
                                           const float* const (&asp)[MT],
                                           const uint8_t* const (&bp)[2],
                                           const float* const (&wsp)[2],
-                                          char (&lds)[2][MT * 32 * ROW8], int nk, int ld_r,
-                                          int ld_c, int lane) {
+                                          char (&lds)[2][MT * 32 * ROW8], int nk,
+                                          int64_t sstride, int ld_r, int ld_c, int lane) {
   constexpr int NA = MT;    // A loads (16 bytes) per thread per stage: BM rows x 8 chunks / 256
   u32x4 areg[NA];
   u32x4 breg[WSLOTS][8];    // [jn][step s][half h]
@@ -114,7 +114,7 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           br[jn * 4 + s * 2 + h] =
-              ld16(bp[jn] + static_cast<int64_t>(kt) * BLK8 + s * 512 + h * 1024);
+              ld16(bp[jn] + static_cast<int64_t>(kt) * sstride + s * 512 + h * 1024);
   };
   auto load_scales = [&](int slot, int kt) {
 #pragma unroll
@@ -254,6 +254,9 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
     const float* asp[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) asp[i] = p.as + static_cast<int64_t>(src_row(i * 32 + lr)) * KB;
+    // packed weights are slab-major: one 128-deep slab of every block of every
+    // group, then the next slab
+    const int64_t sstride = static_cast<int64_t>(p.e_count) * NB16 * BLK8;
     const uint8_t* bp[2];
     const float* wsp[2];
 #pragma unroll
@@ -262,8 +265,7 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
       const float* sbase = (GATED && jn == 1) ? p.s1 : p.s0;
       const int frow = GATED ? n0 + wave * 32 : n0 + wave * 64 + jn * 32;  // fragment's first row
       const int blk = min((frow + lr) >> 4, NB16 - 1);
-      bp[jn] = base + ((static_cast<int64_t>(e) * NB16 + blk) * KB) * BLK8 + (lr & 15) * 16 +
-               hh * 256;
+      bp[jn] = base + (static_cast<int64_t>(e) * NB16 + blk) * BLK8 + (lr & 15) * 16 + hh * 256;
       wsp[jn] = sbase + (static_cast<int64_t>(e) * NB128 + min(frow >> 7, NB128 - 1)) * KB;
     }
 
@@ -277,10 +279,10 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
     static_assert(MT == 4, "one tile height");
     {
       switch (nm) {
-        case 1: a8_k_loop<MT, 1, GATED>(acc, ap, asp, bp, wsp, lds, nk, ld_r, ld_c, lane); break;
-        case 2: a8_k_loop<MT, 2, GATED>(acc, ap, asp, bp, wsp, lds, nk, ld_r, ld_c, lane); break;
-        case 3: a8_k_loop<MT, 3, GATED>(acc, ap, asp, bp, wsp, lds, nk, ld_r, ld_c, lane); break;
-        default: a8_k_loop<MT, 4, GATED>(acc, ap, asp, bp, wsp, lds, nk, ld_r, ld_c, lane); break;
+        case 1: a8_k_loop<MT, 1, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
+        case 2: a8_k_loop<MT, 2, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
+        case 3: a8_k_loop<MT, 3, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
+        default: a8_k_loop<MT, 4, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
       }
     }
 

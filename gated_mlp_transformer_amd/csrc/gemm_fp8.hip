@@ -20,7 +20,10 @@
 // to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 with a unit scale), each slab is
 // accumulated on MFMA in fp32 from zero, and
 // the slab sum is scaled by its block's fp32 scale into the running fp32 sum.
-// The next slab's loads are issued before the current slab is consumed.
+// The next slab's loads are issued before the current slab is consumed; the
+// block scales of a pass are loaded once, one slab per lane, so that inside
+// the slab loop the only memory accesses are the weight and A loads and the
+// in-order load counter waits for exactly the slab being consumed.
 // Experts with more than 16 rows are processed 16 rows at a time (the weights
 // are re-read per pass; decode shapes need one pass).
 //
@@ -127,15 +130,17 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
     // workgroup barrier inside the item loop).
     if (n0w >= p.N) continue;
 
-    // Packed fp8 weights: 16-row x 128-column blocks of 2 KB, [half][lane][16 B];
-    // lane l's two 16-byte loads of a block are row l%16, bytes 32(l/16) + 0..31
-    // of the block's 128-byte slab, each load one contiguous 1 KB across lanes.
+    // Packed fp8 weights: 16-row x 128-column blocks of 2 KB, [half][lane][16 B],
+    // slab-major ([slab][group][row block]); lane l's two 16-byte loads of a
+    // block are row l%16, bytes 32(l/16) + 0..31 of the block's 128-byte slab,
+    // each load one contiguous 1 KB across lanes.
+    const int64_t slab_stride = static_cast<int64_t>(p.e_count) * (p.N / 16) * 2048;
     const uint8_t* wp[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const uint8_t* base = (GATED && q >= QH) ? p.b1 : p.b0;
       const int nb = (n0w >> 4) + (q % QH);
-      wp[q] = base + ((static_cast<int64_t>(e) * (p.N / 16) + nb) * kslabs) * 2048 + lane * 16;
+      wp[q] = base + (static_cast<int64_t>(e) * (p.N / 16) + nb) * 2048 + lane * 16;
     }
     const int64_t sbase = (static_cast<int64_t>(e) * (p.N / SLAB) + n0w / SLAB) * kslabs;
     const float* sp0 = p.s0 + sbase;
@@ -144,6 +149,8 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
     for (int m0 = beg; m0 < end; m0 += 16) {
       const int rows_valid = min(16, end - m0);
       const bool arow_ok = lr < rows_valid;
+      // rows past the valid ones re-read row m0: an output row depends on its
+      // own A row only, and those rows are never stored
       int arow = m0 + (arow_ok ? lr : 0);
       if (p.a_rows != nullptr) arow = clampi(p.a_rows[arow], 0, p.a_src_rows - 1);
       const char* ap = p.a + static_cast<int64_t>(arow) * K * 2 + 64 * lg;
@@ -152,25 +159,27 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int q = 0; q < R; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      SlabRegs<R> cur, nxt;
       auto load = [&](SlabRegs<R>& s, int kb) {
         const int64_t kofs = static_cast<int64_t>(kb) * SLAB;
-        const int64_t bofs = static_cast<int64_t>(kb) * 2048;
+        const int64_t bofs = static_cast<int64_t>(kb) * slab_stride;
 #pragma unroll
         for (int q = 0; q < R; ++q) {
           s.b[q][0] = ld16(wp[q] + bofs);
           s.b[q][1] = ld16(wp[q] + bofs + 1024);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          s.a[c] = arow_ok ? ld16(ap + kofs * 2 + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < 4; ++c) s.a[c] = ld16(ap + kofs * 2 + 16 * c);
       };
-
-      load(cur, 0);
-      for (int kb = 0; kb < kslabs; ++kb) {
-        if (kb + 1 < kslabs) load(nxt, kb + 1);
-        const float sc0 = sp0[kb];
-        const float sc1 = GATED ? sp1[kb] : 0.f;
+      // Block scales of a chunk of up to 64 slabs: lane l holds slab kc + l's,
+      // read in the loop with a uniform lane index, so the slab loop issues no
+      // memory access besides the weight and A loads (one in-order counter
+      // covers all vector loads: a later scale load would hold every
+      // prefetched slab ahead of it)
+      float scl0 = 0.f, scl1 = 0.f;
+      auto compute = [&](const SlabRegs<R>& cur, int j) {
+        const float sc0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scl0), j));
+        const float sc1 = GATED ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scl1), j))
+                                : 0.f;
 #pragma unroll
         for (int q = 0; q < R; ++q) {
           f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -185,7 +194,35 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(sc, sa[r], acc[q][r]);
         }
-        cur = nxt;
+      };
+
+      // Two register sets in turn; the next slab's loads are issued before
+      // the current slab is consumed. Slab counts are even (K % 256 == 0) and
+      // the last pair is peeled, so every wait in the loop is static.
+      // (A scheduling barrier after each group of loads keeps the compiler
+      // from sinking them below the MFMAs they are meant to run under.)
+      SlabRegs<R> r0, r1;
+      for (int kc = 0; kc < kslabs; kc += 64) {
+        const int nks = min(64, kslabs - kc);
+        if (lane < nks) {
+          scl0 = sp0[kc + lane];
+          if (GATED) scl1 = sp1[kc + lane];
+        }
+        load(r0, kc);
+        __builtin_amdgcn_sched_barrier(0);
+        int j = 0;
+        for (; j + 2 < nks; j += 2) {
+          load(r1, kc + j + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(r0, j);
+          load(r0, kc + j + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(r1, j + 1);
+        }
+        load(r1, kc + j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(r0, j);
+        compute(r1, j + 1);
       }
 
       // lane holds output columns 4*lg..4*lg+3 of sub-tile q for row lr.

@@ -89,8 +89,9 @@ size_t packed_weights_bytes(int64_t groups, int32_t N, int32_t K, int32_t dtype)
  *     dst[g][nb][kb][l][v] = W[g][32 nb + l % 32][16 kb + 8 (l / 32) + v]
  *     (l = 0..63, v = 0..7; rows >= N read as 0). Requires K % 16 == 0.
  *   MF_FP8_E4M3 (codes; block scales are not packed): 16-row x 128-column
- *     blocks of 2 KB, each two 1 KB halves:
- *     dst[g][nb][kb][h][l][b] = W[g][16 nb + l % 16][128 kb + 32 (l / 16) + 16 h + b]
+ *     blocks of 2 KB, each two 1 KB halves, 128-column slab major (a packed
+ *     tensor is therefore not sliced by group: pack each group set on its own):
+ *     dst[kb][g][nb][h][l][b] = W[g][16 nb + l % 16][128 kb + 32 (l / 16) + 16 h + b]
  *     (h = 0..1, l = 0..63, b = 0..15; rows >= N read as 0). Requires K % 128 == 0.
  */
 int pack_weights(const void* src, void* dst, int64_t groups, int32_t N, int32_t K,

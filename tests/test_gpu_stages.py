@@ -247,7 +247,8 @@ def _pack_reference(w: np.ndarray, fp8: bool) -> np.ndarray:
         rows = (np.arange(nb)[:, None, None, None, None] * 16 + (l % 16)[None, None, None, :, None])
         cols = (np.arange(K // 128)[None, :, None, None, None] * 128 + 32 * (l // 16)[None, None, None, :, None]
                 + 16 * h[None, None, :, None, None] + b[None, None, None, None, :])
-        return wp[:, rows, cols]
+        # [G, nb, kb, h, l, b] -> slab-major [kb, G, nb, h, l, b]
+        return wp[:, rows, cols].transpose(2, 0, 1, 3, 4, 5)
     v = np.arange(8)
     rows = np.arange(nb)[:, None, None, None] * 32 + (l % 32)[None, None, :, None]
     cols = (np.arange(K // 16)[None, :, None, None] * 16 + 8 * (l // 32)[None, None, :, None]
