@@ -257,6 +257,7 @@ int check_a8(const void* a, const float* a_scale, const int32_t* offsets, int32_
   if (row_index && (src_rows < 1 || src_rows > kI32Max)) return MF_EINVAL;
   if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
   if (K % 256 != 0 || N % 256 != 0) return MF_EUNSUPPORTED;
+  if (K > 16384) return MF_EUNSUPPORTED;  // weight-scale table of a tile: 128 slabs
   if (max_rows == 0) {  // zero-size buffers may be NULL
     *empty = true;
     return MF_OK;

@@ -28,8 +28,9 @@
 // row_index) is loaded one stage ahead and staged in LDS (two buffers, rows of
 // 128 bytes, 16-byte chunks XOR-swizzled by row); weight fragments come
 // straight from global memory into registers three stages ahead (a ring of
-// four slots); the activation and weight scales of the next stage are loaded
-// with it. The fp8 weights use the same packed order as the decode kernels
+// four slots). The activation scales travel with the A rows into LDS; the
+// weight scales of a tile's whole contraction are put in LDS at the tile's
+// start. The fp8 weights use the same packed order as the decode kernels
 // (16-row x 128-column blocks, slab-major, pack.hip); a lane gathers its 32
 // bytes of a 32-row fragment from the two 16-row blocks.
 //
@@ -44,6 +45,7 @@ namespace mf {
 namespace {
 
 constexpr int ROW8 = 128;   // bytes of one A row per stage (a 128-deep block)
+constexpr int A8_MAX_SLABS = 128;  // K <= 16384 (checked by the entry points)
 constexpr int MAXG = 256;
 constexpr int WSLOTS = 4;   // weight register slots: three stages in flight
 constexpr int BLK8 = 2048;  // bytes of one packed 16 x 128 fp8 block
@@ -84,27 +86,33 @@ __device__ __forceinline__ i32x8 join(const u32x4& lo, const u32x4& hi) {
 
 }  // namespace
 
-// K loop of one tile for NM live 32-row sub-tiles. Stage t: issue A(t+1), its
-// activation scales, the weights of t+3 and the weight scales of t+1; for each
-// sub-tile read its two 64-deep fragments from LDS, run two MFMAs per weight
-// fragment from zero and add the block into the result with the block's
-// scales; write A(t+1) to the other LDS buffer; barrier.
+// K loop of one tile for NM live 32-row sub-tiles. Stage t: issue A(t+1) with
+// the activation scales of the rows this thread moves, and the weights of
+// t+3; for each sub-tile read its two 64-deep fragments from LDS, run two
+// MFMAs per weight fragment from zero and add the block into the result with
+// the block's scales (activation scale from LDS beside the A rows, weight
+// scale from the tile's LDS table); write A(t+1) and its scales to the other
+// LDS buffer; barrier. Every scale is consumed together with the data it
+// travels with, so the one in-order load counter never holds a weight
+// prefetch back for a scale, and the four-stage loop body has no branches
+// (a two-stage tail takes nk % 4 == 2), so every wait is static.
 template <int MT, int NM, bool GATED>
 __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* const (&ap)[MT],
-                                          const float* const (&asp)[MT],
-                                          const uint8_t* const (&bp)[2],
-                                          const float* const (&wsp)[2],
-                                          char (&lds)[2][MT * 32 * ROW8], int nk,
-                                          int64_t sstride, int ld_r, int ld_c, int lane) {
+                                          const float* const (&aspr)[MT],
+                                          const uint8_t* const (&bp)[2], const float* s_sw,
+                                          char (&lds)[2][MT * 32 * ROW8],
+                                          float (&s_sa)[2][MT * 32], int nk, int64_t sstride,
+                                          int ld_r, int ld_c, int lane) {
   constexpr int NA = MT;    // A loads (16 bytes) per thread per stage: BM rows x 8 chunks / 256
   u32x4 areg[NA];
+  float ascl[NA];           // activation scales of the rows this thread moves
   u32x4 breg[WSLOTS][8];    // [jn][step s][half h]
-  float sa[2][NM];          // activation scales of this lane's rows, current / next stage
-  float sw[2][2];           // weight scales of the two fragments, current / next stage
   const int lr = lane & 31, hh = lane >> 5;
   auto load_a = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) areg[i] = ld16(ap[i] + static_cast<int64_t>(kt) * ROW8);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ascl[i] = aspr[i][kt];
   };
   auto load_b = [&](u32x4 (&br)[8], int kt) {
 #pragma unroll
@@ -116,21 +124,18 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
           br[jn * 4 + s * 2 + h] =
               ld16(bp[jn] + static_cast<int64_t>(kt) * sstride + s * 512 + h * 1024);
   };
-  auto load_scales = [&](int slot, int kt) {
-#pragma unroll
-    for (int i = 0; i < NM; ++i) sa[slot][i] = asp[i][kt];
-#pragma unroll
-    for (int jn = 0; jn < 2; ++jn) sw[slot][jn] = wsp[jn][kt];
-  };
   auto write_a = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) st16(&lds[buf][swz8(ld_r + 32 * i, ld_c)], areg[i]);
+    // the eight threads of a row store the same value
+#pragma unroll
+    for (int i = 0; i < NA; ++i) s_sa[buf][ld_r + 32 * i] = ascl[i];
   };
-  auto stage = [&](const u32x4 (&br)[8], int buf, int cur, int kt_next, u32x4 (&b_dst)[8],
+  auto stage = [&](const u32x4 (&br)[8], int buf, int kt, int kt_next, u32x4 (&b_dst)[8],
                    int kt_b) {
     load_a(kt_next);
-    load_scales(cur ^ 1, kt_next);
     load_b(b_dst, kt_b);
+    const float sw0 = s_sw[kt], sw1 = s_sw[nk + kt];
     const i32x8 w00 = join(br[0], br[1]), w01 = join(br[2], br[3]);
     const i32x8 w10 = join(br[4], br[5]), w11 = join(br[6], br[7]);
 #pragma unroll
@@ -143,8 +148,9 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
       f32x16 p1 = mfma_fp8(w10, a0, f32x16{});
       p0 = mfma_fp8(w01, a1, p0);
       p1 = mfma_fp8(w11, a1, p1);
-      const float c0 = sa[cur][i] * sw[cur][0];
-      const float c1 = sa[cur][i] * sw[cur][1];
+      const float sa = s_sa[buf][r];
+      const float c0 = sa * sw0;
+      const float c1 = sa * sw1;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         acc[i][0][v] = fmaf(p0[v], c0, acc[i][0][v]);
@@ -155,23 +161,27 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
   };
 
   load_a(0);
-  load_scales(0, 0);
 #pragma unroll
   for (int s = 0; s < WSLOTS - 1; ++s) load_b(breg[s], s < nk ? s : nk - 1);
   write_a(0);
   __syncthreads();
 #define MF_A8_STEP(S)                                                                      \
-  if (kt + (S) < nk) {                                                                     \
+  {                                                                                        \
     const int t_ = kt + (S);                                                               \
-    stage(breg[(S)], (S) & 1, (S) & 1, min(t_ + 1, nk - 1), breg[((S) + WSLOTS - 1) % WSLOTS], \
+    stage(breg[(S)], (S) & 1, t_, min(t_ + 1, nk - 1), breg[((S) + WSLOTS - 1) % WSLOTS],  \
           min(t_ + WSLOTS - 1, nk - 1));                                                   \
     __syncthreads();                                                                       \
   }
-  for (int kt = 0; kt < nk; kt += WSLOTS) {
+  int kt = 0;
+  for (; kt + WSLOTS <= nk; kt += WSLOTS) {
     MF_A8_STEP(0)
     MF_A8_STEP(1)
     MF_A8_STEP(2)
     MF_A8_STEP(3)
+  }
+  if (kt < nk) {  // nk is even: two stages left
+    MF_A8_STEP(0)
+    MF_A8_STEP(1)
   }
 #undef MF_A8_STEP
 }
@@ -180,6 +190,8 @@ template <int MT, bool GATED>
 __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
   constexpr int BN_OUT = GATED ? 128 : 256;
   __shared__ __attribute__((aligned(16))) char lds[2][MT * 32 * ROW8];
+  __shared__ float s_sa[2][MT * 32];           // activation scales of the staged A rows
+  __shared__ float s_sw[4][2 * A8_MAX_SLABS];  // per wave: weight scales of its two fragments
   __shared__ int s_tile0[MAXG + 1];
   __shared__ int s_beg[MAXG];
   __shared__ int s_end[MAXG];
@@ -251,9 +263,9 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       ap[i] = p.a + static_cast<int64_t>(src_row(ld_r + 32 * i)) * Kb + ld_c * 16;
-    const float* asp[MT];
+    const float* aspr[MT];  // activation scale rows of the A rows this thread moves
 #pragma unroll
-    for (int i = 0; i < MT; ++i) asp[i] = p.as + static_cast<int64_t>(src_row(i * 32 + lr)) * KB;
+    for (int i = 0; i < MT; ++i) aspr[i] = p.as + static_cast<int64_t>(src_row(ld_r + 32 * i)) * KB;
     // packed weights are slab-major: one 128-deep slab of every block of every
     // group, then the next slab
     const int64_t sstride = static_cast<int64_t>(p.e_count) * NB16 * BLK8;
@@ -276,13 +288,19 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
       for (int jn = 0; jn < 2; ++jn) acc[i][jn] = f32x16{};
 
     __syncthreads();  // the previous tile's LDS reads are done
+    // this wave's weight scales for the whole contraction, [fragment][slab]
+    // (read back by this wave only, in order)
+    for (int j = lane; j < KB; j += kWave) {
+      s_sw[wave][j] = wsp[0][j];
+      s_sw[wave][KB + j] = wsp[1][j];
+    }
     static_assert(MT == 4, "one tile height");
     {
       switch (nm) {
-        case 1: a8_k_loop<MT, 1, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
-        case 2: a8_k_loop<MT, 2, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
-        case 3: a8_k_loop<MT, 3, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
-        default: a8_k_loop<MT, 4, GATED>(acc, ap, asp, bp, wsp, lds, nk, sstride, ld_r, ld_c, lane); break;
+        case 1: a8_k_loop<MT, 1, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        case 2: a8_k_loop<MT, 2, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        case 3: a8_k_loop<MT, 3, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        default: a8_k_loop<MT, 4, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
       }
     }
 

@@ -309,7 +309,8 @@ int quantize_fp8_rows(const void* x, int64_t rows, const int32_t* row_count, int
  * Each 128-deep block of the contraction is summed exactly on the fp8 MFMA
  * (fp32 accumulation) and added into the fp32 result scaled by its activation
  * and weight scales; SiLU(g)*u in fp32 in the epilogue.
- * Requires 1 <= e_count <= 256, d % 256 == 0, f % 256 == 0.
+ * Requires 1 <= e_count <= 256, d % 256 == 0, f % 256 == 0, d <= 16384
+ * (MF_EUNSUPPORTED otherwise).
  */
 int grouped_gate_up_a8(const void* xq, const float* x_scale, const int32_t* row_index,
                        int64_t src_rows, const int32_t* offsets, int32_t e_count,
@@ -323,7 +324,7 @@ int grouped_gate_up_a8(const void* xq, const float* x_scale, const int32_t* row_
  * hq [max_rows, f] codes and h_scale [max_rows, f/128] f32 (quantize_fp8_rows
  * of grouped_gate_up_a8's bf16 H), w_down [e_count, d, f] packed E4M3FN codes,
  * s_down [e_count, d/128, f/128] f32, y_perm [max_rows, d] bf16 out.
- * Same requirements as grouped_gate_up_a8.
+ * Same requirements as grouped_gate_up_a8, with f <= 16384 (the contraction).
  */
 int grouped_down_a8(const void* hq, const float* h_scale, const int32_t* offsets,
                     int32_t e_count, int64_t max_rows, int32_t f, int32_t d, const void* w_down,

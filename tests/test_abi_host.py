@@ -173,6 +173,7 @@ def test_fp8_prefill_validation(lib):
     assert gu(ec=257) == MF_EUNSUPPORTED
     assert gu(d=384) == MF_EUNSUPPORTED           # d % 256
     assert gu(f=128) == MF_EUNSUPPORTED           # f % 256
+    assert gu(d=16640) == MF_EUNSUPPORTED         # contraction above 128 slabs of 128
     assert gu(xq=ctypes.c_void_p(0x100008)) == MF_EUNSUPPORTED
     assert gu(rows=0, xq=N, xs=N, h=N) == MF_OK   # zero rows: nothing to do
 
@@ -184,6 +185,7 @@ def test_fp8_prefill_validation(lib):
     assert dn(sd=N) == MF_EINVAL
     assert dn(y=N) == MF_EINVAL
     assert dn(f=640) == MF_EUNSUPPORTED
+    assert dn(f=16640) == MF_EUNSUPPORTED
     assert dn(rows=0, hq=N, hs=N, y=N) == MF_OK
 
 
