@@ -92,6 +92,8 @@ def _oracle_w(W, e):
     ([0, 0, 0], 256, 256),
     ([1, 33, 65, 97, 128, 129, 31, 32], 256, 256),     # every tail sub-tile count
     ([300] * 3 + [0, 77, 513] + [300] * 4, 1024, 512),  # several tiles and rounds
+    ([5, 40, 0, 33], 768, 256),   # gate/up: six stages (a four-stage body and a tail)
+    ([7, 64], 256, 768),          # down: six stages
 ])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_a8(g, counts, d, f, gather):
