@@ -21,14 +21,19 @@
 //
 // Operand paths. A wave's weight fragments are private to it and come straight
 // from global memory into registers. The A tile is shared by the four waves
-// and goes through LDS (two buffers; 64-byte rows whose 16-byte chunks are
-// XOR-swizzled so that both the row writes and the 32-row fragment reads are
-// bank-conflict free).
+// and goes through LDS (four stage buffers; 64-byte rows whose 16-byte chunks
+// are XOR-swizzled so that both the row writes and the 32-row fragment reads
+// are bank-conflict free). A moves two stages at a time, as whole 128-byte
+// row segments (eight threads per row): the L1's outstanding misses bound this
+// kernel's loads (its L1 waits on L2 data half the time), and a 64-byte
+// access holds a whole 128-byte line slot, so half-line A loads cost twice the
+// miss slots of the bytes they move.
 //
 // Pipeline. BK = 32 per stage (two MFMA k-steps). Weight fragments are loaded
 // three stages ahead into four register slots that rotate through a K loop
-// unrolled by four, so every slot index is a compile-time constant; A is
-// loaded two stages ahead into two register buffers. The loop is branch-free
+// unrolled by four, so every slot index is a compile-time constant; each
+// even stage loads the A pair two stages ahead, the next (odd) stage writes
+// it into the pair's two LDS buffers. The loop is branch-free
 // (prefetch indices are clamped), so the compiler's vmcnt waits track exactly
 // the loads being consumed. Within a stage the instruction order is fixed
 // with scheduling groups: the stage's first-k-step fragments are read from
@@ -108,22 +113,33 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f
 // prefetch stage indices are clamped (the last steps re-load the final stage),
 // so the compiler's vmcnt waits track exactly the loads being consumed.
 //
-// Stage t: issue A(t+2) and the weights of t+3, run the MFMAs of t, write
-// A(t+1) (loaded during stage t-1) into the other LDS buffer, barrier.
-// Thread (ld_r, ld_c) moves chunk ld_c of rows ld_r + 64i, i < ceil(NM/2).
+// Stage t: (t even) issue the A pair t+2, t+3; issue the weights of t+3; run
+// the MFMAs of t; (t odd) write the A pair loaded at stage t-1 into its two
+// LDS buffers; barrier. Thread (ld_r, ld_c) moves 16-byte chunk ld_c of the
+// 128-byte pair segment of rows ld_r + 32i, i < NM.
 template <int MT, int NM>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* const (&ap)[MT / 2],
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
+                                       const int (&arow)[MT], int64_t Kb,
                                        const char* const (&bp)[2],
-                                       char (&lds)[2][MT * 32 * ROWB], int nk, int ld_r,
+                                       char (&lds)[4][MT * 32 * ROWB], int nk, int ld_r,
                                        int ld_c, int lane) {
-  constexpr int NA = (NM + 1) / 2;  // A loads per thread per stage
-  u32x4 areg[2][NA];
-  u32x4 breg[SLOTS][4];  // [fragment column jn * 2 + k-step s]
+  // A moves two stages at a time as whole 128-byte row segments (eight
+  // threads per row, rows ld_r + 32 i): chunk ld_c & 3 of stage pair member
+  // ld_c >> 2. Loaded at even stages, written at the next odd stage into the
+  // two LDS buffers of the pair.
+  constexpr int NA = NM;
+  u32x4 areg[NA];
+  u32x4 breg[SLOTS][4];
   const int lr = lane & 31, lg = lane >> 5;
-  auto load_a = [&](u32x4 (&ar)[NA], int kt) {
+  auto load_pair = [&](int kt) {  // stages kt and kt + 1 (kt even)
     const int64_t ka = static_cast<int64_t>(kt) * ROWB;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ar[i] = ld16(ap[i] + ka);
+    for (int i = 0; i < NA; ++i) areg[i] = ld16(abase + static_cast<int64_t>(arow[i]) * Kb + ka);
+  };
+  auto write_pair = [&](int buf0) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      st16(&lds[(buf0 + (ld_c >> 2)) & 3][swz(ld_r + 32 * i, ld_c & 3)], areg[i]);
   };
   auto load_b = [&](u32x4 (&br)[4], int kt) {
     const int64_t kb = static_cast<int64_t>(kt) * (2 * FRAG);
@@ -132,19 +148,16 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* const (
 #pragma unroll
       for (int s = 0; s < 2; ++s) br[jn * 2 + s] = ld16(bp[jn] + kb + s * FRAG);
   };
-  auto write_a = [&](const u32x4 (&ar)[NA], int buf) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) st16(&lds[buf][swz(ld_r + 64 * i, ld_c)], ar[i]);
-  };
   // One stage in a fixed instruction order. The k-step 0 fragments of every
-  // live sub-tile are read first. The global loads of later stages (A two
-  // stages ahead, weights three) and k-step 1's fragment reads are spread
-  // between k-step 0's MFMAs, one load per MFMA pair, so that the address
-  // queue never backs up into the MFMA issue. The next stage's A tile is
-  // written to the other LDS buffer between k-step 1's MFMAs.
-  auto stage = [&](const u32x4 (&br)[4], int buf, const u32x4 (&next_a)[NA],
-                   u32x4 (&a_dst)[NA], int kt_a, u32x4 (&b_dst)[4], int kt_b) {
-    load_a(a_dst, kt_a);
+  // live sub-tile are read from LDS first; the global loads (the weights of
+  // three stages ahead and, at even stages, the A pair two stages ahead) and
+  // k-step 1's fragment reads are spread between k-step 0's MFMAs, one load
+  // per MFMA pair, so the address queue never backs up into the MFMA issue; at
+  // odd stages the pair loaded one stage earlier is written to LDS between
+  // k-step 1's MFMAs.
+  auto stage = [&](const u32x4 (&br)[4], int buf, bool even, int kt_pair, u32x4 (&b_dst)[4],
+                   int kt_b) {
+    if (even) load_pair(kt_pair);
     load_b(b_dst, kt_b);
     u32x4 af[2][NM];
 #pragma unroll
@@ -158,37 +171,49 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* const (
         acc[i][0] = mfma32(br[s], af[s][i], acc[i][0]);
         acc[i][1] = mfma32(br[2 + s], af[s][i], acc[i][1]);
       }
-    write_a(next_a, buf ^ 1);
+    if (!even) write_pair((buf + 1) & 3);
     // masks: MFMA 0x008, VMEM read 0x020, DS read 0x100, DS write 0x200
-    constexpr int NL = NA + 4;                       // global loads of the stage
-    constexpr int LEAD = NL > NM ? NL - NM : 0;      // loads that do not fit between pairs
-    __builtin_amdgcn_sched_group_barrier(0x020, LEAD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
+    if (even) {
+      constexpr int NLE = NA + 4, LE = NLE > NM ? NLE - NM : 0;
+      __builtin_amdgcn_sched_group_barrier(0x020, LE, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < NL - LEAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < NLE - LE) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);
+    } else {
+      constexpr int NLO = 4, LO = NLO > NM ? NLO - NM : 0;
+      __builtin_amdgcn_sched_group_barrier(0x020, LO, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < NLO - LO) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * (NM - NA), 0);
   };
 
-  load_a(areg[0], 0);
-  load_a(areg[1], 1 < nk ? 1 : nk - 1);
+  // the weights of stages 0..2 and the first A pair, same outstanding order
+  // at the loop entry as at its back-edge (A pair, then weights)
+  load_pair(0);
 #pragma unroll
   for (int s = 0; s < PREF; ++s) load_b(breg[s], s < nk ? s : nk - 1);
-  write_a(areg[0], 0);
+  write_pair(0);
   __syncthreads();
 #define MF_GEMM_STEP(S)                                                                    \
   {                                                                                        \
     const int t_ = kt + (S);                                                               \
-    stage(breg[(S)], (S) & 1, areg[((S) + 1) & 1], areg[(S) & 1], min(t_ + 2, nk - 1),      \
-          breg[((S) + PREF) % SLOTS], min(t_ + PREF, nk - 1));                             \
+    stage(breg[(S)], (S), ((S) & 1) == 0, min(t_ + 2, nk - 2), breg[((S) + PREF) % SLOTS],  \
+          min(t_ + PREF, nk - 1));                                                         \
     __syncthreads();                                                                       \
   }
   for (int kt = 0; kt < nk; kt += SLOTS) {
@@ -204,7 +229,7 @@ template <int MT, bool GATED, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   constexpr int BM = MT * 32;
   constexpr int BN_OUT = GATED ? 128 : 256;
-  __shared__ __attribute__((aligned(16))) char lds[2][BM * ROWB];
+  __shared__ __attribute__((aligned(16))) char lds[4][BM * ROWB];
   __shared__ int s_tile0[MAX_GROUPS + 1];
   __shared__ int s_beg[MAX_GROUPS];
   __shared__ int s_end[MAX_GROUPS];
@@ -247,8 +272,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int lr = lane & 31, lg = lane >> 5;
-  const int ld_c = tid & 3;    // A: 16-byte chunk this thread moves
-  const int ld_r = tid >> 2;   // A: first row this thread moves (then +64, +128, ...)
+  const int ld_c = tid & 7;    // A: 16-byte chunk of a two-stage (128-byte) row segment
+  const int ld_r = tid >> 3;   // A: first row this thread moves (then +32, +64, ...)
   const int G = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int nk = p.kc / BK;
@@ -283,14 +308,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     // ---- per-thread global pointers ---------------------------------------
     // A rows past the tile's valid rows re-read row0 (row m of the result
     // depends on row m of A only, and those rows are never stored).
-    const char* ap[MT / 2];
+    int arow[MT];  // source rows of the rows ld_r + 32 i this thread moves
 #pragma unroll
-    for (int i = 0; i < MT / 2; ++i) {
-      const int r = ld_r + 64 * i;
-      int arow = row0 + (r < rows_valid ? r : 0);
-      if (p.a_rows != nullptr) arow = clampi(p.a_rows[arow], 0, p.a_src_rows - 1);
-      ap[i] = p.a + static_cast<int64_t>(arow) * Kb + kofs_a + ld_c * 16;
+    for (int i = 0; i < MT; ++i) {
+      const int r = ld_r + 32 * i;
+      int ar = row0 + (r < rows_valid ? r : 0);
+      if (p.a_rows != nullptr) ar = clampi(p.a_rows[ar], 0, p.a_src_rows - 1);
+      arow[i] = ar;
     }
+    const char* abase = p.a + kofs_a + ld_c * 16;
     const char* bp[2];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
@@ -310,22 +336,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     __syncthreads();  // the previous tile's LDS reads are done
     if constexpr (MT == 8) {
       switch (nm) {
-        case 1: k_loop<MT, 1>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 2: k_loop<MT, 2>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 3: k_loop<MT, 3>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 4: k_loop<MT, 4>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 5: k_loop<MT, 5>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 6: k_loop<MT, 6>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 7: k_loop<MT, 7>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        default: k_loop<MT, 8>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 1: k_loop<MT, 1>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 4: k_loop<MT, 4>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 5: k_loop<MT, 5>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 6: k_loop<MT, 6>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 7: k_loop<MT, 7>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 8>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
       }
     } else {
       static_assert(MT == 4, "MT is 4 or 8");
       switch (nm) {
-        case 1: k_loop<MT, 1>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 2: k_loop<MT, 2>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 3: k_loop<MT, 3>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
-        default: k_loop<MT, 4>(acc, ap, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 1: k_loop<MT, 1>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 4>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
       }
     }
 
