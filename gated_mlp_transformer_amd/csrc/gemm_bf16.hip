@@ -22,12 +22,14 @@
 // Operand paths. A wave's weight fragments are private to it and come straight
 // from global memory into registers. The A tile is shared by the four waves
 // and goes through LDS (four stage buffers; 64-byte rows whose 16-byte chunks
-// are XOR-swizzled so that both the row writes and the 32-row fragment reads
-// are bank-conflict free). A moves two stages at a time, as whole 128-byte
-// row segments (eight threads per row): the L1's outstanding misses bound this
-// kernel's loads (its L1 waits on L2 data half the time), and a 64-byte
-// access holds a whole 128-byte line slot, so half-line A loads cost twice the
-// miss slots of the bytes they move.
+// are XOR-swizzled so that the 32-row fragment reads are bank-conflict free).
+// A moves two stages at a time, as whole 128-byte row segments (eight threads
+// per row): the L1's outstanding misses bound this kernel's loads (its L1
+// waits on L2 data half the time), and a 64-byte access holds a whole 128-byte
+// line slot, so half-line A loads cost twice the miss slots of the bytes they
+// move. (The two halves of a segment go to two stage buffers that map to the
+// same banks, a two-way conflict on those writes; a mapping without it
+// measured no faster.)
 //
 // Pipeline. BK = 32 per stage (two MFMA k-steps). Weight fragments are loaded
 // three stages ahead into four register slots that rotate through a K loop
@@ -38,9 +40,9 @@
 // the loads being consumed. Within a stage the instruction order is fixed
 // with scheduling groups: the stage's first-k-step fragments are read from
 // LDS, then every pair of MFMAs is followed by one second-k-step fragment read
-// and one global load, then the next stage's A tile is written to the other
-// LDS buffer between the remaining MFMAs. Spreading the loads keeps the
-// address queue from stalling the MFMA issue.
+// and one global load, and at odd stages the A pair loaded one stage earlier
+// is written to its two LDS buffers between the remaining MFMAs. Spreading the
+// loads keeps the address queue from stalling the MFMA issue.
 //
 // Schedule. Group boundaries come from the device-side offsets (or, in the
 // masked layout, from per-group counts within fixed blocks of cap rows), so
