@@ -10,6 +10,11 @@ intermediate 2048, 32 of 256 experts local, Zipf-skewed router bias, bf16).
 Inputs and weights are resident in HBM before the timed region. W untimed
 warm-up steps, then exactly K steps between two device synchronisations;
 HIP events on the launch stream bracket every stage of every timed step.
+The warm-up default is long enough for the clock to settle after the idle
+time of input generation: the first few tens of steps after it run slower.
+The same step is then also timed as a HIP graph (the forward captured once
+and replayed, W + K replays), each replay checked to reproduce the eager
+output bit for bit (`graph_ms_per_step`).
 
 Prints ONE JSON line: tokens/s of the whole step, the roofline of the
 dominant kernel (the grouped gate/up GEMM, against the bf16 MFMA peak), the
@@ -49,7 +54,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the decode (contiguous and masked) / fp8-activation prefill / "
@@ -162,6 +167,42 @@ def time_layer(layer, x, steps, warmup):
     return ms, us, wall
 
 
+def time_layer_graph(layer, x, steps, warmup):
+    """The same step as a HIP graph: one forward captured (no marks), replayed
+    `warmup` times untimed, then exactly `steps` replays timed. The replays must
+    reproduce the eager forward bit for bit (checked before and after timing)."""
+    import torch
+    ref = layer(x).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = layer(x)
+    torch.cuda.synchronize()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("bench: graph replay differs from the eager forward")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(steps):
+        graph.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("bench: graph replay differs from the eager forward")
+    ms = t_start.elapsed_time(t_end) / steps
+    del graph
+    return ms
+
+
 def build_layer(spec, device, seed=0):
     import gated_mlp_transformer_amd as g
     from synth.workloads import make_moe
@@ -183,17 +224,20 @@ def run_moe(name, steps, warmup):
     log(f"[bench] {name}: building inputs")
     layer, inp = build_layer(spec, "cuda")
     ms, us, wall = time_layer(layer, inp["x"], steps, warmup)
+    ms_graph = time_layer_graph(layer, inp["x"], steps, warmup)
     S = int(layer.counts.sum().item())  # both layouts (offsets are unused when masked)
     active = int((layer.counts > 0).sum().item())
     counts = layer.counts.cpu()
     welt = 2 if spec["wdtype"] == "bf16" else 1
     work = moe_work(spec["T"], spec["d"], spec["f"], spec["E"], 8, S, active, spec["e_count"],
                     welt, act_fp8=spec.get("act_fp8", False))
-    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, S={S}, active experts {active}")
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, {ms_graph * 1e3:.1f} us as a graph, "
+        f"S={S}, active experts {active}")
     info = dict(slots=S, active_experts=active,
                 count_min=int(counts.min()), count_max=int(counts.max()),
                 count_mean=round(float(counts.float().mean()), 1))
-    return dict(spec=spec, layer=layer, inp=inp, ms=ms, us=us, wall=wall, work=work, info=info)
+    return dict(spec=spec, layer=layer, inp=inp, ms=ms, ms_graph=ms_graph, us=us, wall=wall,
+                work=work, info=info)
 
 
 def run_dense(steps, warmup):
@@ -357,6 +401,7 @@ def main():
             res = run_moe(name, args.steps, args.warmup)
             peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
+                                  graph_ms_per_step=res["ms_graph"],
                                   stages=stage_report(res["work"], res["us"], peak), **res["info"]),
                              default=str), flush=True)
         elif args.only == "dense":
@@ -381,6 +426,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(res["ms"], 4),
+        # the same step captured once as a HIP graph and replayed (checked bit for
+        # bit against the eager step)
+        "graph_ms_per_step": round(res["ms_graph"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -410,7 +458,8 @@ def main():
         gemm_bytes = dec["work"]["grouped_gate_up"]["bytes"] + dec["work"]["grouped_down"]["bytes"]
         gemm_us = dec["us"]["grouped_gate_up"] + dec["us"]["grouped_down"]
         line["decode"] = {"workload": DECODE, "tokens_per_s": round(64 / (dec["ms"] * 1e-3), 1),
-                          "ms_per_step": round(dec["ms"], 4), **dec["info"],
+                          "ms_per_step": round(dec["ms"], 4),
+                          "graph_ms_per_step": round(dec["ms_graph"], 4), **dec["info"],
                           "grouped_gemm_hbm_frac": round(
                               gemm_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                           "stages": dstage}
@@ -419,7 +468,7 @@ def main():
         dm = run_moe(DECODE_MASKED, max(10, args.steps // 2), args.warmup)
         line["decode_masked"] = {
             "workload": DECODE_MASKED, "tokens_per_s": round(64 / (dm["ms"] * 1e-3), 1),
-            "ms_per_step": round(dm["ms"], 4),
+            "ms_per_step": round(dm["ms"], 4), "graph_ms_per_step": round(dm["ms_graph"], 4),
             "vs_contiguous_step": round(line["decode"]["ms_per_step"] / dm["ms"], 4),
             "stages": stage_report(dm["work"], dm["us"])}
         del dm
@@ -429,7 +478,8 @@ def main():
         gus = p8["us"]["grouped_gate_up"] + p8["us"]["grouped_down"]
         line["prefill_fp8_activations"] = {
             "workload": PREFILL_FP8, "tokens_per_s": round(T / (p8["ms"] * 1e-3), 1),
-            "ms_per_step": round(p8["ms"], 4), **p8["info"],
+            "ms_per_step": round(p8["ms"], 4), "graph_ms_per_step": round(p8["ms_graph"], 4),
+            **p8["info"],
             # the GEMM stages include the activation quantisation that feeds them
             "grouped_gemm_fp8_mfma_frac": round(gw / (gus * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
             "stages": stage_report(p8["work"], p8["us"], PEAK_FP8_TFLOPS)}
