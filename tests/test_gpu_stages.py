@@ -300,6 +300,8 @@ def _oracle_weights(W, e, wdtype):
     ("bf16", [300] * 5 + [0, 77, 513] + [300] * 8, 1024, 1024),  # > 256 tiles: several rounds
     ("fp8", [1, 3, 0, 17, 2, 16], 256, 512),
     ("fp8", [40], 512, 256),
+    ("bf16", [(7 * e) % 5 for e in range(256)], 256, 256),   # the most groups (256)
+    ("bf16", [3, 40], 8192, 256),     # the longest contraction: 256 K stages
     ("fp8", [3, 17, 2], 256, 8448),   # down contraction of 66 slabs: two scale chunks
     ("fp8", [9, 0, 4], 8448, 256),    # gate/up contraction of 66 slabs
 ])
