@@ -36,7 +36,8 @@
 //
 // Schedule. As the bf16 grouped GEMM: each expert's rows split into
 // near-equal chunks of at most MT 32-row sub-tiles, tiles numbered expert /
-// chunk / n-tile, persistent grid with XCD-contiguous round-robin.
+// n-tile / chunk (the chunks sharing a weight n-tile consecutive), persistent
+// grid with XCD-contiguous round-robin.
 #include "common.h"
 #include "launch.h"
 
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
     }
     const int e = lo;
     const int t = L - s_tile0[e];
-    const int mi = t / NT, ni = t - mi * NT;
     const int sub_e = (s_end[e] - s_beg[e] + 31) >> 5;
     const int nch = (sub_e + MT - 1) / MT;
+    const int ni = t / nch, mi = t - ni * nch;  // n-tile major, chunk minor
     const int q = sub_e / nch, r = sub_e - q * nch;
     const int z0 = mi * q + min(mi, r);
     const int nm = q + (mi < r ? 1 : 0);

@@ -49,12 +49,17 @@
 // no host sync is needed. Each workgroup computes the schedule itself: group e's
 // ceil(rows_e / 32) sub-tiles are split into ceil(sub_e / MT) near-equal
 // chunks (so an expert's last chunk is not a sliver), a tile is one chunk
-// against one n-tile, and tiles are numbered group-major, then chunk, then
-// n-tile, so the n-tiles that share one A chunk are consecutive. A tile runs a
-// K loop instantiated for its live sub-tiles only. The grid is persistent;
-// workgroup b (dispatched round-robin to XCD b % 8) takes tile
+// against one n-tile, and tiles are numbered group-major, then n-tile, then
+// chunk, so the chunks that share one weight n-tile are consecutive. A tile
+// runs a K loop instantiated for its live sub-tiles only. The grid is
+// persistent; workgroup b (dispatched round-robin to XCD b % 8) takes tile
 // it*G + (b%8)*(G/8) + b/8 in round it, so each XCD works on a contiguous run
-// of tiles at a time and A chunks and weight tiles are shared through its L2.
+// of tiles at a time and shares weight n-tiles and A chunks through its L2.
+// With the chunk minor, a group's run of tiles that straddles two XCDs (or
+// two rounds) splits its n-tiles between them, so each weight n-tile is still
+// fetched once and only the (smaller) A chunks are fetched twice; with the
+// n-tile minor, both sides fetched every n-tile (prefill routing: 1.60 GB of
+// L2 misses per gate/up launch against 1.20 GB of algorithmic traffic).
 #include "common.h"
 #include "launch.h"
 
@@ -297,9 +302,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     }
     const int e = lo;
     const int t = L - s_tile0[e];
-    const int mi = t / NT, ni = t - mi * NT;
     const int sub_e = (s_end[e] - s_beg[e] + 31) >> 5;
     const int nch = (sub_e + Z - 1) / Z;
+    const int ni = t / nch, mi = t - ni * nch;  // n-tile major, chunk minor
     const int q = sub_e / nch, r = sub_e - q * nch;
     const int z0 = mi * q + min(mi, r);            // first sub-tile of the chunk
     const int nm = q + (mi < r ? 1 : 0);           // sub-tiles in the chunk

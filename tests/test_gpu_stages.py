@@ -65,7 +65,8 @@ def test_rmsnorm_in_place(g):
 
 @pytest.mark.parametrize("T,d,E", [(1, 256, 8), (37, 256, 12), (300, 256, 64), (257, 512, 256),
                                    (64, 4096, 256), (1000, 1024, 200), (4096, 768, 9),
-                                   (129, 2048, 100)])
+                                   (129, 2048, 100), (5000, 1024, 256), (2000, 2048, 160),
+                                   (600, 768, 256)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
     idx, w = g.moe_route(r["x"], g.pack_weights(r["w_r"]), r["bias"])
