@@ -72,3 +72,26 @@ def test_measured_traffic_follows_the_source_hash(bench, tmp_path, monkeypatch):
     assert bench.measured_traffic("k", "p.md") is None
     src.unlink()
     assert bench.measured_traffic("k", "p.md") is None
+
+
+def _run_bench(*args, env_extra=None):
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=300, env=env)
+
+
+def test_bench_refuses_several_gpus():
+    r = _run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_bench_has_no_cpu_fallback():
+    # with no GPU visible the benchmark stops instead of timing anything on the host
+    r = _run_bench("--steps", "1", "--warmup", "0", env_extra={"HIP_VISIBLE_DEVICES": "-1",
+                                                               "CUDA_VISIBLE_DEVICES": "-1"})
+    assert r.returncode == 1
+    assert "no GPU visible" in r.stderr and r.stdout == ""
