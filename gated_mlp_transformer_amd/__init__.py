@@ -70,6 +70,7 @@ def _s(stream) -> ctypes.c_void_p:
 
 
 def _dev(*ts: Optional[torch.Tensor]) -> None:
+    cur = None
     for t in ts:
         if t is None:
             continue
@@ -77,6 +78,20 @@ def _dev(*ts: Optional[torch.Tensor]) -> None:
             raise ValueError("libmoeffn takes device tensors only")
         if not t.is_contiguous():
             raise ValueError("libmoeffn takes contiguous tensors only")
+        cur = torch.cuda.current_device() if cur is None else cur
+        if t.device.index != cur:
+            raise ValueError(f"libmoeffn: tensors must be on the current device (cuda:{cur}), "
+                             f"got {t.device}")
+
+
+def _need(name: str, what: str, t: Optional[torch.Tensor], shape, dtype) -> None:
+    """t (if given) must have exactly `shape` and `dtype`: the kernels write and
+    read whole buffers of those sizes, with no size passed for most of them."""
+    if t is None:
+        return
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: {what} must be {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
 
 
 def _ok(name: str, status: int) -> None:
@@ -93,9 +108,11 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
     if out is None:
         out = torch.empty_like(x)
     _dev(x, gamma, out)
-    if gamma.dtype != x.dtype or out.dtype != x.dtype or x.dim() != 2:
+    if x.dim() != 2:
         raise ValueError("rmsnorm: x [T, d], gamma [d], out [T, d] of one dtype")
     T, d = x.shape
+    _need("rmsnorm", "gamma", gamma, (d,), x.dtype)
+    _need("rmsnorm", "out", out, (T, d), x.dtype)
     _ok("rmsnorm", _lib.load().rmsnorm(_p(x), _p(gamma), _p(out), T, d, eps,
                                        _dtype_code(x.dtype), _s(stream)))
     return out
@@ -154,6 +171,8 @@ def moe_route(x: torch.Tensor, w_r: torch.Tensor, bias: torch.Tensor, k: int = 8
         raise ValueError("moe_route: x, w_r bf16 and bias f32")
     if w_r.groups != 1 or w_r.K != d or tuple(bias.shape) != (E,):
         raise ValueError("moe_route: w_r [E, d], bias [E]")
+    _need("moe_route", "topk_idx", topk_idx, (T, k), torch.int32)
+    _need("moe_route", "topk_w", topk_w, (T, k), torch.float32)
     _ok("moe_route", _lib.load().moe_route(
         _p(x), _p(w_r.data), _p(bias), T, d, E, k, _p(topk_idx), _p(topk_w), _p(workspace),
         workspace.numel() * workspace.element_size(), _s(stream)))
@@ -196,6 +215,12 @@ def moe_permute(topk_idx: torch.Tensor, e_begin: int, e_count: int,
     _dev(topk_idx, x, x_perm, counts, offsets, src_token, inv_pos, workspace)
     if topk_idx.dtype != i32:
         raise ValueError("moe_permute: topk_idx must be int32")
+    for what, t, shape in (("counts", counts, (e_count,)), ("offsets", offsets, (e_count + 1,)),
+                           ("src_token", src_token, (T * k,)), ("inv_pos", inv_pos, (T, k))):
+        _need("moe_permute", what, t, shape, i32)
+    if x is not None:
+        _need("moe_permute", "x", x, (T, d), x.dtype)
+        _need("moe_permute", "x_perm", x_perm, (T * k, d), x.dtype)
     _ok("moe_permute", _lib.load().moe_permute(
         _p(topk_idx), T, k, e_begin, e_count, _p(x), d, xdt, _p(x_perm), _p(counts),
         _p(offsets), _p(src_token), _p(inv_pos), _p(workspace),
@@ -226,6 +251,9 @@ def moe_dispatch_masked(topk_idx: torch.Tensor, e_begin: int, e_count: int, cap:
     _dev(topk_idx, counts, row_index, pos, workspace)
     if topk_idx.dtype != i32:
         raise ValueError("moe_dispatch_masked: topk_idx must be int32")
+    for what, t, shape in (("counts", counts, (e_count,)), ("row_index", row_index, (e_count * cap,)),
+                           ("pos", pos, (T, k))):
+        _need("moe_dispatch_masked", what, t, shape, i32)
     _ok("moe_dispatch_masked", _lib.load().moe_dispatch_masked(
         _p(topk_idx), T, k, e_begin, e_count, cap, _p(counts), _p(row_index), _p(pos),
         _p(workspace), workspace.numel() * workspace.element_size(), _s(stream)))
@@ -241,11 +269,15 @@ def grouped_gate_up_masked(x: torch.Tensor, row_index: torch.Tensor, counts: tor
     e_count, f = w_gate.groups, w_gate.N
     if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
         raise ValueError("grouped_gate_up_masked: w_gate/w_up [E, f, d]")
-    if row_index.numel() != e_count * cap or counts.numel() != e_count:
-        raise ValueError("grouped_gate_up_masked: row_index [E*cap], counts [E]")
+    n = "grouped_gate_up_masked"
+    _need(n, "x", x, (src_rows, d), torch.bfloat16)
+    _need(n, "row_index", row_index, (e_count * cap,), torch.int32)
+    _need(n, "counts", counts, (e_count,), torch.int32)
     wdt = _grouped_dtype(w_gate, w_up)
+    _block_scales(n, wdt, e_count, f, d, s_gate=s_gate, s_up=s_up)
     if h_out is None:
         h_out = torch.empty((e_count * cap, f), dtype=torch.bfloat16, device=x.device)
+    _need(n, "h_out", h_out, (e_count * cap, f), torch.bfloat16)
     _dev(x, row_index, counts, s_gate, s_up, h_out)
     _ok("grouped_gate_up_masked", _lib.load().grouped_gate_up_masked(
         _p(x), _p(row_index), src_rows, _p(counts), cap, e_count, d, f, _p(w_gate.data),
@@ -261,14 +293,29 @@ def grouped_down_masked(h: torch.Tensor, counts: torch.Tensor, cap: int, w_down,
     e_count, d = w_down.groups, w_down.N
     if w_down.K != f or rows != e_count * cap:
         raise ValueError("grouped_down_masked: h [E*cap, f], w_down [E, d, f]")
+    n = "grouped_down_masked"
+    _need(n, "h", h, (rows, f), torch.bfloat16)
+    _need(n, "counts", counts, (e_count,), torch.int32)
     wdt = _grouped_dtype(w_down)
+    _block_scales(n, wdt, e_count, d, f, s_down=s_down)
     if y_perm is None:
         y_perm = torch.empty((rows, d), dtype=torch.bfloat16, device=h.device)
+    _need(n, "y_perm", y_perm, (rows, d), torch.bfloat16)
     _dev(h, counts, s_down, y_perm)
     _ok("grouped_down_masked", _lib.load().grouped_down_masked(
         _p(h), _p(counts), cap, e_count, f, d, _p(w_down.data), wdt, _p(s_down), _p(y_perm),
         _s(stream)))
     return y_perm
+
+
+def _block_scales(name: str, wdt: int, e_count: int, N: int, K: int, **scales) -> None:
+    """fp8 weights need their [e_count, N/128, K/128] f32 block scales."""
+    if wdt != MF_FP8_E4M3:
+        return
+    for what, t in scales.items():
+        if t is None:
+            raise ValueError(f"{name}: fp8 weights need {what}")
+        _need(name, what, t, (e_count, N // 128, K // 128), torch.float32)
 
 
 def _grouped_rows(x: torch.Tensor, row_index, name: str):
@@ -295,13 +342,18 @@ def grouped_swiglu(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.Te
     if (d2 != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d)
             or (w_down.groups, w_down.N, w_down.K) != (e_count, d, f)):
         raise ValueError("grouped_swiglu: w_gate/w_up [E, f, d], w_down [E, d, f]")
-    if offsets.numel() != e_count + 1 or offsets.dtype != torch.int32:
-        raise ValueError("grouped_swiglu: offsets [E+1] int32")
+    n = "grouped_swiglu"
+    _need(n, "offsets", offsets, (e_count + 1,), torch.int32)
+    _need(n, "x_perm", x_perm, (x_perm.shape[0], d), torch.bfloat16)
     wdt = _grouped_dtype(w_gate, w_up, w_down)
+    _block_scales(n, wdt, e_count, f, d, s_gate=s_gate, s_up=s_up)
+    _block_scales(n, wdt, e_count, d, f, s_down=s_down)
     if h_work is None:
         h_work = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=x_perm.device)
+    _need(n, "h_work", h_work, (max_rows, f), torch.bfloat16)
+    _need(n, "y_perm", y_perm, (max_rows, d), torch.bfloat16)
     _dev(x_perm, row_index, offsets, s_gate, s_up, s_down, h_work, y_perm)
     _ok("grouped_swiglu", _lib.load().grouped_swiglu(
         _p(x_perm), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
@@ -332,9 +384,14 @@ def grouped_gate_up(x_perm: torch.Tensor, offsets: torch.Tensor, w_gate: torch.T
     e_count, f = w_gate.groups, w_gate.N
     if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
         raise ValueError("grouped_gate_up: w_gate/w_up [E, f, d]")
+    n = "grouped_gate_up"
+    _need(n, "offsets", offsets, (e_count + 1,), torch.int32)
+    _need(n, "x_perm", x_perm, (x_perm.shape[0], d), torch.bfloat16)
     wdt = _grouped_dtype(w_gate, w_up)
+    _block_scales(n, wdt, e_count, f, d, s_gate=s_gate, s_up=s_up)
     if h_out is None:
         h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=x_perm.device)
+    _need(n, "h_out", h_out, (max_rows, f), torch.bfloat16)
     _dev(x_perm, row_index, offsets, s_gate, s_up, h_out)
     _ok("grouped_gate_up", _lib.load().grouped_gate_up(
         _p(x_perm), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
@@ -350,9 +407,14 @@ def grouped_down(h: torch.Tensor, offsets: torch.Tensor, w_down: torch.Tensor, s
     e_count, d = w_down.groups, w_down.N
     if w_down.K != f:
         raise ValueError("grouped_down: w_down [E, d, f]")
+    n = "grouped_down"
+    _need(n, "offsets", offsets, (e_count + 1,), torch.int32)
+    _need(n, "h", h, (max_rows, f), torch.bfloat16)
     wdt = _grouped_dtype(w_down)
+    _block_scales(n, wdt, e_count, d, f, s_down=s_down)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=h.device)
+    _need(n, "y_perm", y_perm, (max_rows, d), torch.bfloat16)
     _dev(h, offsets, s_down, y_perm)
     _ok("grouped_down", _lib.load().grouped_down(
         _p(h), _p(offsets), e_count, max_rows, f, d, _p(w_down.data), wdt, _p(s_down), _p(y_perm),
@@ -371,6 +433,10 @@ def quantize_fp8_rows(x: torch.Tensor, *, row_count=None, q=None, scales=None, s
         q = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, max(K // 128, 0)), dtype=torch.float32, device=x.device)
+    n = "quantize_fp8_rows"
+    _need(n, "q", q, (rows, K), torch.uint8)
+    _need(n, "scales", scales, (rows, max(K // 128, 0)), torch.float32)
+    _need(n, "row_count", row_count, (1,), torch.int32)
     _dev(x, row_count, q, scales)
     _ok("quantize_fp8_rows", _lib.load().quantize_fp8_rows(_p(x), rows, _p(row_count), K, _p(q),
                                                            _p(scales), _s(stream)))
@@ -395,10 +461,14 @@ def grouped_gate_up_a8(xq: torch.Tensor, x_scale: torch.Tensor, offsets: torch.T
     e_count, f = w_gate.groups, w_gate.N
     if w_gate.K != d or (w_up.groups, w_up.N, w_up.K) != (e_count, f, d):
         raise ValueError("grouped_gate_up_a8: w_gate/w_up [E, f, d]")
-    if xq.dtype != torch.uint8 or x_scale.shape != (xq.shape[0], d // 128):
-        raise ValueError("grouped_gate_up_a8: xq uint8 [rows, d], x_scale [rows, d/128]")
+    n = "grouped_gate_up_a8"
+    _need(n, "xq", xq, (xq.shape[0], d), torch.uint8)
+    _need(n, "x_scale", x_scale, (xq.shape[0], d // 128), torch.float32)
+    _need(n, "offsets", offsets, (e_count + 1,), torch.int32)
+    _block_scales(n, MF_FP8_E4M3, e_count, f, d, s_gate=s_gate, s_up=s_up)
     if h_out is None:
         h_out = torch.empty((max_rows, f), dtype=torch.bfloat16, device=xq.device)
+    _need(n, "h_out", h_out, (max_rows, f), torch.bfloat16)
     _dev(xq, x_scale, row_index, offsets, s_gate, s_up, h_out)
     _ok("grouped_gate_up_a8", _lib.load().grouped_gate_up_a8(
         _p(xq), _p(x_scale), _p(row_index), src_rows, _p(offsets), e_count, max_rows, d, f,
@@ -415,10 +485,14 @@ def grouped_down_a8(hq: torch.Tensor, h_scale: torch.Tensor, offsets: torch.Tens
     e_count, d = w_down.groups, w_down.N
     if w_down.K != f:
         raise ValueError("grouped_down_a8: w_down [E, d, f]")
-    if hq.dtype != torch.uint8 or h_scale.shape != (max_rows, f // 128):
-        raise ValueError("grouped_down_a8: hq uint8 [rows, f], h_scale [rows, f/128]")
+    n = "grouped_down_a8"
+    _need(n, "hq", hq, (max_rows, f), torch.uint8)
+    _need(n, "h_scale", h_scale, (max_rows, f // 128), torch.float32)
+    _need(n, "offsets", offsets, (e_count + 1,), torch.int32)
+    _block_scales(n, MF_FP8_E4M3, e_count, d, f, s_down=s_down)
     if y_perm is None:
         y_perm = torch.empty((max_rows, d), dtype=torch.bfloat16, device=hq.device)
+    _need(n, "y_perm", y_perm, (max_rows, d), torch.bfloat16)
     _dev(hq, h_scale, offsets, s_down, y_perm)
     _ok("grouped_down_a8", _lib.load().grouped_down_a8(
         _p(hq), _p(h_scale), _p(offsets), e_count, max_rows, f, d, _p(w_down.data), _p(s_down),
@@ -436,6 +510,11 @@ def moe_combine(y_perm: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tenso
         out = torch.empty((T, d), dtype=out_dtype, device=y_perm.device)
     if residual is not None and (residual.shape != out.shape or residual.dtype != out.dtype):
         raise ValueError("moe_combine: residual must match out in shape and dtype")
+    n = "moe_combine"
+    _need(n, "y_perm", y_perm, (max_rows, d), torch.bfloat16)
+    _need(n, "inv_pos", inv_pos, (T, k), torch.int32)
+    _need(n, "topk_w", topk_w, (T, k), torch.float32)
+    _need(n, "out", out, (T, d), out.dtype)
     _dev(y_perm, inv_pos, topk_w, residual, out)
     _ok("moe_combine", _lib.load().moe_combine(_p(y_perm), _p(inv_pos), _p(topk_w), T, k, d,
                                                max_rows, _p(residual), _p(out),
@@ -464,6 +543,11 @@ def tp_shard_mlp(x: torch.Tensor, w_gate_s: torch.Tensor, w_up_s: torch.Tensor,
         h_work = torch.empty((T, fs), dtype=x.dtype, device=x.device)
     if partial is None:
         partial = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _need("tp_shard_mlp", "h_work", h_work, (T, fs), x.dtype)
+    _need("tp_shard_mlp", "partial", partial, (T, d), torch.float32)
+    if x.dtype == torch.float32:
+        for what, w in (("w_gate_s", w_gate_s), ("w_up_s", w_up_s), ("w_down_s", w_down_s)):
+            _need("tp_shard_mlp", what, w, tuple(w.shape), torch.float32)
     _dev(x, *ptrs, h_work, partial)
     _ok("tp_shard_mlp", _lib.load().tp_shard_mlp(
         _p(x), _p(ptrs[0]), _p(ptrs[1]), _p(ptrs[2]), T, d, fs, _dtype_code(x.dtype),

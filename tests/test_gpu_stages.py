@@ -423,3 +423,34 @@ def test_tp_shard_bf16(g, T, d, f, p):
         assert_fp(f"partial {i}", to_f64(part), ref)
         total = total + to_f64(part)
     assert_fp("sum of partials", total, oracle.swiglu(xf, wg, wu, wd))
+
+
+# ------------------------------------------------------- binding argument checks --
+
+def test_binding_rejects_wrong_buffers(g):
+    """Undersized outputs, wrong index dtypes and missing fp8 scales are refused
+    before anything is enqueued (the kernels would otherwise run past them)."""
+    T, d, f, E = 64, 256, 256, 4
+    x = torch.zeros((T, d), dtype=torch.bfloat16, device=DEV)
+    w = g.pack_weights(torch.zeros((E, f, d), dtype=torch.bfloat16, device=DEV))
+    wd = g.pack_weights(torch.zeros((E, d, f), dtype=torch.bfloat16, device=DEV))
+    offsets = torch.tensor([0, 16, 32, 48, 64], dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="h_out"):
+        g.grouped_gate_up(x, offsets, w, w, h_out=torch.empty((T - 1, f), dtype=torch.bfloat16,
+                                                             device=DEV))
+    with pytest.raises(ValueError, match="offsets"):
+        g.grouped_gate_up(x, offsets.long(), w, w)
+    with pytest.raises(ValueError, match="y_perm"):
+        g.grouped_down(torch.zeros((T, f), dtype=torch.bfloat16, device=DEV), offsets, wd,
+                       y_perm=torch.empty((T, d - 64), dtype=torch.bfloat16, device=DEV))
+    w8 = g.pack_weights(torch.zeros((E, f, d), dtype=torch.float8_e4m3fn, device=DEV))
+    with pytest.raises(ValueError, match="need s_gate"):
+        g.grouped_gate_up(x, offsets, w8, w8)
+    idx = torch.zeros((T, 8), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="inv_pos"):
+        g.moe_permute(idx, 0, E, inv_pos=torch.empty((T, 4), dtype=torch.int32, device=DEV))
+    with pytest.raises(ValueError, match="out"):
+        g.moe_combine(torch.zeros((T * 8, d), dtype=torch.bfloat16, device=DEV), idx,
+                      torch.zeros((T, 8), dtype=torch.float32, device=DEV),
+                      out=torch.empty((T // 2, d), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
