@@ -639,6 +639,9 @@ class MoEFFNLayer:
     def forward(self, x: torch.Tensor, stream=None, marks=None,
                 residual: Optional[torch.Tensor] = None) -> torch.Tensor:
         s = torch.cuda.current_stream() if stream is None else stream
+        if tuple(x.shape) != (self.T, self.d) or x.dtype != torch.bfloat16:
+            raise ValueError(f"MoEFFNLayer: x must be bf16 {(self.T, self.d)} (the shape the "
+                             f"layer's buffers were sized for), got {x.dtype} {tuple(x.shape)}")
 
         def mark(i):
             if marks is not None:
