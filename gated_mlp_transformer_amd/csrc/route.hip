@@ -14,11 +14,10 @@
 //     ascending); the ids are emitted ascending with w = s / sum(s).
 //     A round takes the wave-wide maximum of the keys (mapped to
 //     order-preserving unsigned integers) with DPP max steps at register
-//     speed, then the lowest expert id
-//     that holds it from the wave's ballots of key == max: a lane holds
-//     experts lane + 64c, so the first slot c with a match and its lowest
-//     lane give the id. Only that candidate is retired, so equal keys are
-//     taken in ascending id order over the rounds.
+//     speed, then the lowest expert id that holds it as a second DPP
+//     maximum (of 256 - id over the lanes' candidates equal to the key
+//     maximum; a lane holds experts lane + 64c). Only that candidate is
+//     retired, so equal keys are taken in ascending id order over the rounds.
 #include "common.h"
 #include "launch.h"
 
@@ -109,53 +108,50 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     sc[c] = sigmoidf_(z);
     key[c] = e < E ? order_key(sc[c] + bias[min(e, E - 1)]) : 0u;
   }
-  int sel[8];
-  float ssel[8];
+  // Eight rounds; a round takes the wave-wide maximum key m, then the lowest
+  // expert id holding it as a second wave-wide maximum, of 256 - e over each
+  // lane's candidates equal to m (all in VALU/DPP: no ballot chains on the
+  // CU's one scalar unit, which all the resident token waves share). The
+  // owner lane retires the winner and flags it.
+  uint32_t won = 0;  // bit c: expert lane + 64c was selected
 #pragma unroll
   for (int round = 0; round < 8; ++round) {
     const uint32_t m = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
-    uint64_t hit[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) hit[c] = __builtin_amdgcn_ballot_w64(key[c] == m);
-    const int cw = hit[0] ? 0 : hit[1] ? 1 : hit[2] ? 2 : 3;  // uniform
-    const uint64_t hw = cw == 0 ? hit[0] : cw == 1 ? hit[1] : cw == 2 ? hit[2] : hit[3];
-    const int lw = __builtin_ctzll(hw);
-    const float sv = cw == 0 ? sc[0] : cw == 1 ? sc[1] : cw == 2 ? sc[2] : sc[3];
-    sel[round] = 64 * cw + lw;
-    ssel[round] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), lw));
+    uint32_t cand = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (c == cw && lane == lw) key[c] = 0u;  // the owner lane retires the winner
-  }
-  // ids ascending (I is a set), scores carried along
+      cand = max(cand, key[c] == m ? 256u - static_cast<uint32_t>(lane + 64 * c) : 0u);
+    const int e = 256 - static_cast<int>(wave_umax(cand));
 #pragma unroll
-  for (int a = 1; a < 8; ++a) {
-#pragma unroll
-    for (int b = a; b > 0; --b) {
-      if (sel[b - 1] > sel[b]) {
-        const int ti = sel[b];
-        sel[b] = sel[b - 1];
-        sel[b - 1] = ti;
-        const float ts = ssel[b];
-        ssel[b] = ssel[b - 1];
-        ssel[b - 1] = ts;
-      }
+    for (int c = 0; c < 4; ++c) {
+      const bool hit = lane + 64 * c == e;  // only the owner lane's slot matches
+      key[c] = hit ? 0u : key[c];
+      won |= hit ? 1u << c : 0u;
     }
   }
-  float sum = 0.f;
+  // The winners in ascending id order (slot c, then lane): rank r goes to
+  // lane r of the outputs, and the scores are summed in that order.
+  int out_e = 0;
+  float out_s = 0.f, sum = 0.f;
+  int r = 0;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) sum += ssel[q];
-  if (lane < 8) {
-    int mine = sel[0];
-    float ms = ssel[0];
-#pragma unroll
-    for (int q = 1; q < 8; ++q)
-      if (lane == q) {
-        mine = sel[q];
-        ms = ssel[q];
+  for (int c = 0; c < 4; ++c) {
+    uint64_t mk = __builtin_amdgcn_ballot_w64((won >> c) & 1u);
+    while (mk) {
+      const int l = __builtin_ctzll(mk);
+      mk &= mk - 1;
+      const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[c]), l));
+      if (lane == r) {
+        out_e = l + 64 * c;
+        out_s = sv;
       }
-    idx_out[t * 8 + lane] = mine;
-    w_out[t * 8 + lane] = ms / sum;
+      sum += sv;
+      ++r;
+    }
+  }
+  if (lane < 8) {
+    idx_out[t * 8 + lane] = out_e;
+    w_out[t * 8 + lane] = out_s / sum;
   }
 }
 
