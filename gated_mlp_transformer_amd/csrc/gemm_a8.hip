@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
   const int NB128 = p.N / 128;
 
   // device-side schedule: expert e's ceil(rows/32) sub-tiles in ceil(sub/MT)
-  // near-equal chunks; tiles numbered expert / chunk / n-tile
+  // near-equal chunks; tiles numbered expert / n-tile / chunk
   int ntile = 0;
   if (tid < p.e_count) {
     const int beg = clampi(p.offsets[tid], 0, p.max_rows);

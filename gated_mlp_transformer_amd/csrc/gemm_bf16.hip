@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   // Group e's rows form sub_e = ceil(rows_e / 32) sub-tiles, split into
   // nch_e = ceil(sub_e / Z) near-equal chunks (the first sub_e % nch_e one
   // sub-tile longer). A tile is one chunk against one n-tile; tiles are
-  // numbered group-major, then chunk, then n-tile.
+  // numbered group-major, then n-tile, then chunk.
   constexpr int Z = MT;
   int ntile = 0;
   if (tid < p.e_count) {
