@@ -454,3 +454,30 @@ def test_binding_rejects_wrong_buffers(g):
                       torch.zeros((T, 8), dtype=torch.float32, device=DEV),
                       out=torch.empty((T // 2, d), dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
+
+
+def test_zero_tokens_through_every_call(g):
+    """T = 0 is a valid call everywhere: nothing is launched and every output
+    is an empty tensor of the right shape (zero-size buffers may be NULL)."""
+    d, f, E, ec = 256, 256, 16, 4
+    bf = torch.bfloat16
+    x = torch.empty((0, d), dtype=bf, device=DEV)
+    v = g.rmsnorm(x, torch.ones(d, dtype=bf, device=DEV))
+    idx, w = g.moe_route(v, g.pack_weights(torch.zeros((E, d), dtype=bf, device=DEV)),
+                         torch.zeros(E, dtype=torch.float32, device=DEV))
+    res = g.moe_permute(idx, 0, ec)
+    wg, wu = (g.pack_weights(torch.zeros((ec, f, d), dtype=bf, device=DEV)) for _ in range(2))
+    wd = g.pack_weights(torch.zeros((ec, d, f), dtype=bf, device=DEV))
+    h = g.grouped_gate_up(v, res.offsets, wg, wu, row_index=res.src_token)
+    y = g.grouped_down(h, res.offsets, wd)
+    out = g.moe_combine(y, res.inv_pos, w)
+    q, sc = g.quantize_fp8_rows(x)
+    shards = [g.pack_weights(torch.zeros(s, dtype=bf, device=DEV)) for s in ((f, d), (f, d), (d, f))]
+    part, hw = g.tp_shard_mlp(x, *shards)
+    torch.cuda.synchronize()
+    assert v.shape == (0, d) and idx.shape == (0, 8) and w.shape == (0, 8)
+    assert torch.equal(res.counts.cpu(), torch.zeros(ec, dtype=torch.int32))
+    assert torch.equal(res.offsets.cpu(), torch.zeros(ec + 1, dtype=torch.int32))
+    assert h.shape == (0, f) and y.shape == (0, d) and out.shape == (0, d)
+    assert q.shape == (0, d) and sc.shape == (0, d // 128)
+    assert part.shape == (0, d) and hw.shape == (0, f)
