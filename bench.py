@@ -142,8 +142,17 @@ def stage_report(work, us, mfma_peak=PEAK_BF16_TFLOPS):
 # ------------------------------------------------------------------- runners
 
 
+def summary(vals):
+    """mean, median and min of per-rep times (µs)."""
+    import statistics
+    vals = list(vals)
+    return dict(mean=sum(vals) / len(vals), median=statistics.median(vals), min=min(vals))
+
+
 def time_layer(layer, x, steps, warmup):
-    """Warm up, then time exactly `steps` forwards with per-stage events."""
+    """Warm up, then time exactly `steps` forwards back to back with per-stage
+    events. Returns (ms per step over the bracketed region, per-stage lists of
+    µs per step, wall seconds)."""
     import torch
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -161,10 +170,27 @@ def time_layer(layer, x, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_end) / steps
-    us = {}
-    for s, name in enumerate(layer.STAGES):
-        us[name] = 1e3 * sum(m[s].elapsed_time(m[s + 1]) for m in marks) / steps
+    us = {name: [1e3 * m[s].elapsed_time(m[s + 1]) for m in marks]
+          for s, name in enumerate(layer.STAGES)}
+    us["step"] = [1e3 * m[0].elapsed_time(m[6]) for m in marks]
     return ms, us, wall
+
+
+def time_layer_flushed(layer, x, reps, scratch):
+    """`reps` forwards, each preceded by an untimed write of `scratch` (larger
+    than the 256 MB last-level cache, so no operand stays cached from the
+    previous rep). Returns per-stage lists of µs per rep."""
+    import torch
+    stream = torch.cuda.current_stream()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(i & 0x7F)
+        layer(x, marks=marks[i])
+    torch.cuda.synchronize()
+    us = {name: [1e3 * m[s].elapsed_time(m[s + 1]) for m in marks]
+          for s, name in enumerate(layer.STAGES)}
+    us["step"] = [1e3 * m[0].elapsed_time(m[6]) for m in marks]
+    return us
 
 
 def time_layer_graph(layer, x, steps, warmup):
@@ -203,44 +229,48 @@ def time_layer_graph(layer, x, steps, warmup):
     return ms
 
 
-def build_layer(spec, device, seed=0):
+def build_layer(spec, device, seed=0, norm=True):
     import gated_mlp_transformer_amd as g
     from synth.workloads import make_moe
     inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
                    wdtype=spec["wdtype"], zipf=spec["zipf"], seed=seed, device=device)
     layer = g.MoEFFNLayer(T=spec["T"], d=spec["d"], f=spec["f"], w_r=inp["w_r"],
-                          bias=inp["bias"], gamma=inp["gamma"], w_gate=inp["w_gate"],
-                          w_up=inp["w_up"], w_down=inp["w_down"], e_begin=spec["e_begin"],
-                          s_gate=inp.get("s_gate"), s_up=inp.get("s_up"),
-                          s_down=inp.get("s_down"), act_fp8=spec.get("act_fp8", False),
+                          bias=inp["bias"], gamma=inp["gamma"] if norm else None,
+                          w_gate=inp["w_gate"], w_up=inp["w_up"], w_down=inp["w_down"],
+                          e_begin=spec["e_begin"], s_gate=inp.get("s_gate"),
+                          s_up=inp.get("s_up"), s_down=inp.get("s_down"),
+                          act_fp8=spec.get("act_fp8", False),
                           layout=spec.get("layout", "contiguous"))
     return layer, inp
 
 
-def run_moe(name, steps, warmup):
-    import torch
+def run_moe(name, steps, warmup, scratch=None, norm=True, graph=True):
     import synth
     spec = synth.WORKLOADS[name]
-    log(f"[bench] {name}: building inputs")
-    layer, inp = build_layer(spec, "cuda")
+    log(f"[bench] {name}{'' if norm else ' (no rmsnorm)'}: building inputs")
+    layer, inp = build_layer(spec, "cuda", norm=norm)
     ms, us, wall = time_layer(layer, inp["x"], steps, warmup)
-    ms_graph = time_layer_graph(layer, inp["x"], steps, warmup)
+    flushed = time_layer_flushed(layer, inp["x"], steps, scratch) if scratch is not None else None
+    ms_graph = time_layer_graph(layer, inp["x"], steps, warmup) if graph else None
     S = int(layer.counts.sum().item())  # both layouts (offsets are unused when masked)
     active = int((layer.counts > 0).sum().item())
     counts = layer.counts.cpu()
     welt = 2 if spec["wdtype"] == "bf16" else 1
     work = moe_work(spec["T"], spec["d"], spec["f"], spec["E"], 8, S, active, spec["e_count"],
                     welt, act_fp8=spec.get("act_fp8", False))
-    log(f"[bench] {name}: {ms * 1e3:.1f} us/step, {ms_graph * 1e3:.1f} us as a graph, "
-        f"S={S}, active experts {active}")
+    if not norm:
+        work["rmsnorm"] = {}
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step"
+        + (f", {ms_graph * 1e3:.1f} us as a graph" if graph else "")
+        + f", S={S}, active experts {active}")
     info = dict(slots=S, active_experts=active,
                 count_min=int(counts.min()), count_max=int(counts.max()),
                 count_mean=round(float(counts.float().mean()), 1))
     return dict(spec=spec, layer=layer, inp=inp, ms=ms, ms_graph=ms_graph, us=us, wall=wall,
-                work=work, info=info)
+                flushed=flushed, work=work, info=info)
 
 
-def run_dense(steps, warmup):
+def run_dense(steps, warmup, scratch=None):
     """RMSNorm + one bf16 TP shard of the gated MLP (4096 x 4096, f_s 2048)."""
     import torch
     import gated_mlp_transformer_amd as g
@@ -265,24 +295,66 @@ def run_dense(steps, warmup):
         if ev:
             ev[2].record(stream)
 
+    def timed(flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            if flush:
+                scratch.fill_(i & 0x7F)
+            step(evs[i])
+        torch.cuda.synchronize()
+        return ([1e3 * e[0].elapsed_time(e[1]) for e in evs],
+                [1e3 * e[1].elapsed_time(e[2]) for e in evs])
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    norm_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    shard_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    norm_us, shard_us = timed(False)
+    fl = timed(True) if scratch is not None else None
     flops = 6 * T * d * f
-    return dict(workload=DENSE, rmsnorm_us=round(norm_us, 2),
-                rmsnorm_hbm_frac=round((4 * T * d + 2 * d) / (norm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                tp_shard_us=round(shard_us, 2),
-                tp_shard_tflop_s=round(flops / (shard_us * 1e-6) / 1e12, 1),
-                tp_shard_mfma_frac=round(flops / (shard_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4))
+    norm_bytes = 4 * T * d + 2 * d
+    shard_bytes = 2 * T * d + 3 * 2 * d * f + 2 * 2 * T * f + 4 * T * d
+    return dict(workload=DENSE, norm_us=norm_us, shard_us=shard_us, flushed=fl,
+                work={"rmsnorm": dict(bytes=norm_bytes),
+                      "tp_shard_mlp": dict(bytes=shard_bytes, flops=flops)})
 
 
-def run_router(steps, warmup):
+def run_dense_f32(steps, warmup):
+    """The fp32 dense workload: X 16x64, four TP shards of f = 256 (f_s = 64)
+    and the sum of their partials: the latency of the whole sharded MLP."""
+    import torch
+    import gated_mlp_transformer_amd as g
+    import synth
+    from synth.workloads import make_dense, shard_weights
+    spec = synth.WORKLOADS["dense_f32_16x64_f256_p4"]
+    T, d, f, p = spec["T"], spec["d"], spec["f"], spec["p"]
+    D = make_dense(T, d, f, dtype=torch.float32, device="cuda")
+    shards = [shard_weights(D["w_gate"], D["w_up"], D["w_down"], p, i) for i in range(p)]
+    hs = [torch.empty((T, f // p), dtype=torch.float32, device="cuda") for _ in range(p)]
+    parts = [torch.empty((T, d), dtype=torch.float32, device="cuda") for _ in range(p)]
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+
+    def step():
+        for i in range(p):
+            g.tp_shard_mlp(D["x"], *shards[i], h_work=hs[i], partial=parts[i])
+        torch.sum(torch.stack(parts), dim=0, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = [1e3 * a.elapsed_time(b) for a, b in evs]
+    st = summary(us)
+    return dict(workload="dense_f32_16x64_f256_p4", shards=p,
+                us_median=round(st["median"], 2), us_min=round(st["min"], 2),
+                what="4 tp_shard_mlp calls (fp32) + the sum of their partials")
+
+
+def run_router(steps, warmup, scratch=None):
     """Router + index-only permutation over all 256 experts, 4096 tokens."""
     import torch
     import gated_mlp_transformer_amd as g
@@ -295,7 +367,8 @@ def run_router(steps, warmup):
     idx = torch.empty((T, 8), dtype=torch.int32, device="cuda")
     w = torch.empty((T, 8), dtype=torch.float32, device="cuda")
     ws = torch.empty(g.moe_permute_workspace_size(T, 8, E), dtype=torch.uint8, device="cuda")
-    rws = torch.empty(g.moe_route_workspace_size(T, d, E), dtype=torch.uint8, device="cuda")
+    rws = torch.empty(max(1, g.moe_route_workspace_size(T, d, E)), dtype=torch.uint8,
+                      device="cuda")
     bufs = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
                 offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
                 src_token=torch.empty(T * 8, dtype=torch.int32, device="cuda"),
@@ -312,49 +385,138 @@ def run_router(steps, warmup):
         if ev:
             ev[2].record(stream)
 
+    def timed(flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            if flush:
+                scratch.fill_(i & 0x7F)
+            step(evs[i])
+        torch.cuda.synchronize()
+        return ([1e3 * e[0].elapsed_time(e[1]) for e in evs],
+                [1e3 * e[1].elapsed_time(e[2]) for e in evs])
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    route_us = 1e3 * sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    perm_us = 1e3 * sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    route_us, perm_us = timed(False)
+    fl = timed(True) if scratch is not None else None
     rbytes = T * d * 2 + E * d * 2 + E * 4 + T * 8 * 8
-    return dict(workload=ROUTER, route_us=round(route_us, 2),
-                route_hbm_frac=round(rbytes / (route_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                route_tflop_s=round(2 * T * d * E / (route_us * 1e-6) / 1e12, 1),
-                permute_index_us=round(perm_us, 2))
+    return dict(workload=ROUTER, route_us=route_us, perm_us=perm_us, flushed=fl,
+                work={"moe_route": dict(bytes=rbytes, flops=2 * T * d * E),
+                      "moe_permute": dict(bytes=T * 8 * 4 + T * 8 * 8 + (E + 1) * 8)})
+
+
+def measure_attainable(reps=10):
+    """What this GPU sustains, measured here with the library's probes: bf16
+    MFMA FLOP/s with no memory traffic, and HBM read bandwidth over a 4 GiB
+    buffer. Each is the best of `reps` timed launches after warm-up."""
+    import ctypes
+    import torch
+    from gated_mlp_transformer_amd import _lib
+    lib = _lib.load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda")
+    iters = 4000
+    flops = cus * 4 * iters * 16 * 32768
+
+    def best(launch, work):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for _ in range(3):
+            if launch() != 0:
+                raise RuntimeError("bench: probe launch failed")
+        for i in range(reps):
+            ev[i][0].record()
+            launch()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return max(work / (a.elapsed_time(b) * 1e-3) for a, b in ev)
+
+    def mfma():
+        return lib.mf_probe_mfma_bf16(cus, iters, ctypes.c_void_p(out.data_ptr()), s)
+
+    mfma_tf = best(mfma, flops) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+
+    def read(wgs):
+        return lambda: lib.mf_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), wgs,
+                                             ctypes.c_void_p(out.data_ptr()), s)
+
+    hbm = max(best(read(cus * m), buf.numel()) for m in (2, 4, 8)) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return dict(mfma_bf16_tflop_s=round(mfma_tf, 1), hbm_gb_s=round(hbm, 1), cus=cus,
+                source="mf_probe_mfma_bf16 (back-to-back 32x32x16 bf16 MFMA, 4 waves per CU) "
+                       "and mf_probe_hbm_read (16-byte loads over 4 GiB, 2/4/8 workgroups per "
+                       f"CU), best of {reps} launches each")
+
+
+def full_report(work, us, flushed=None, mfma_peak=PEAK_BF16_TFLOPS, attain=None,
+                mfma_attain_key="mfma_bf16_tflop_s"):
+    """Per stage: mean / median / min µs of the back-to-back steps (the mean is
+    what `us` of stage_report states), the median and min of the flushed reps,
+    and the spec-peak and attainable-peak fractions of the median."""
+    out = {}
+    for name, w in work.items():
+        if name not in us:
+            continue
+        st = summary(us[name])
+        r = dict(us=round(st["mean"], 2), us_median=round(st["median"], 2),
+                 us_min=round(st["min"], 2))
+        t = st["median"] * 1e-6
+        if w.get("bytes"):
+            gbs = w["bytes"] / t / 1e9
+            r.update(gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+            if attain:
+                r["hbm_frac_attainable"] = round(gbs / attain["hbm_gb_s"], 4)
+        if w.get("flops"):
+            tf = w["flops"] / t / 1e12
+            r.update(tflop_s=round(tf, 1), mfma_frac=round(tf / mfma_peak, 4))
+            if attain and mfma_attain_key in attain:
+                r["mfma_frac_attainable"] = round(tf / attain[mfma_attain_key], 4)
+        if flushed is not None and name in flushed:
+            fs = summary(flushed[name])
+            r.update(flushed_us_median=round(fs["median"], 2), flushed_us_min=round(fs["min"], 2))
+        out[name] = r
+    return out
 
 
 # ---------------------------------------------------------------- CPU oracle
 
 
-def cpu_baseline(res):
-    """The fp64 oracle on the same prefill step, on this host's cores."""
-    import numpy as np
-    import torch
-    import oracle
+def host_cores():
+    """Cores this process may run on, the machine's count and the BLAS pool."""
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report what the process may use
-        threads = len(os.sched_getaffinity(0))
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [0])
+    except Exception:  # threadpoolctl missing
+        blas = None
+    return dict(cores=cores, cpu_count=os.cpu_count(), blas_threads=blas)
+
+
+def _bits(t):
+    import numpy as np
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline(res):
+    """The fp64 oracle on the same prefill step, on this host's cores (the
+    headline baseline): whole steps, repeated until about 10 s have elapsed."""
+    import numpy as np
+    import oracle
     spec, inp = res["spec"], res["inp"]
-
-    def bits(t):
-        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    host = {k: bits(inp[k]) for k in ("x", "gamma", "w_r", "w_gate", "w_up", "w_down")}
+    hc = host_cores()
+    host = {k: _bits(inp[k]) for k in ("x", "gamma", "w_r", "w_gate", "w_up", "w_down")}
     bias = inp["bias"].cpu().numpy().astype(np.float64)
     T = spec["T"]
-    log(f"[bench] cpu oracle: {T} tokens on {threads} BLAS threads")
+    log(f"[bench] cpu oracle: {PREFILL}, {hc}")
     dec = oracle.bf16_bits_to_f64
     weights = lambda e: (dec(host["w_gate"][e]).T, dec(host["w_up"][e]).T,  # noqa: E731
                          dec(host["w_down"][e]).T)
-    # whole steps, repeated until about 10 s of CPU work have been timed
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.moe_ffn(dec(host["x"]), dec(host["gamma"]), dec(host["w_r"]), bias, weights,
@@ -363,10 +525,87 @@ def cpu_baseline(res):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or reps >= 50:
             break
-    return dict(value=round(reps * T / dt, 1), unit="tokens/s", cores=int(threads),
+    return dict(value=round(reps * T / dt, 1), unit="tokens/s", cores=hc["cores"],
+                cpu_count=hc["cpu_count"], blas_threads=hc["blas_threads"],
                 kind="oracle", seconds=round(dt, 2), steps=reps,
                 sample=f"{reps} full {PREFILL} steps ({T} tokens each), fp64 numpy, incl. bf16 "
                        f"decoding of inputs and all 32 local experts' weights")
+
+
+def cpu_baselines_other(dec_res=None):
+    """The oracle on the other workloads, same host, same run: 3 reps of the
+    dense fp32, dense bf16 and router workloads; one rep of the whole decode
+    workload, streaming each routed expert's dequantisation."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+    from synth.workloads import make_dense, make_router
+    out = {}
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return min(ts), sum(ts) / len(ts)
+
+    dec = oracle.bf16_bits_to_f64
+    # dense fp32, 16 x 64, four shards and their sum
+    D = make_dense(16, 64, 256, dtype=torch.float32)
+    x, wg, wu, wd = (D[k].double().numpy() for k in ("x", "w_gate", "w_up", "w_down"))
+    best, mean = timed(lambda: sum(oracle.tp_shard_mlp(x, wg.T, wu.T, wd.T, 4, i)
+                                   for i in range(4)), 3)
+    out["dense_f32_16x64_f256_p4"] = dict(us_per_rep=round(mean * 1e6, 1), reps=3,
+                                          sample="the whole workload: 4 shards + sum")
+    # dense bf16, 4096 x 4096, RMSNorm + one shard
+    s = synth.WORKLOADS[DENSE]
+    D = make_dense(s["T"], s["d"], s["f"], dtype=torch.bfloat16, norm=True)
+    x, g_, wg, wu, wd = (dec(_bits(D[k])) for k in ("x", "gamma", "w_gate", "w_up", "w_down"))
+    best, mean = timed(lambda: oracle.tp_shard_mlp(oracle.rmsnorm(x, g_), wg.T, wu.T, wd.T, 1, 0),
+                       3)
+    out[DENSE] = dict(value=round(s["T"] / mean, 1), unit="tokens/s", seconds_per_rep=round(mean, 3),
+                      reps=3, sample="the whole workload (4096 tokens): RMSNorm + one shard, fp64")
+    # router, 4096 tokens x 256 experts, route + permutation
+    s = synth.WORKLOADS[ROUTER]
+    r = make_router(s["T"], s["d"], s["E"])
+    x, w_r = dec(_bits(r["x"])), dec(_bits(r["w_r"]))
+    b = r["bias"].double().numpy()
+
+    def route_perm():
+        idx = oracle.route(x, w_r, b)[0]
+        oracle.permute(idx, 0, s["E"])
+
+    best, mean = timed(route_perm, 3)
+    out[ROUTER] = dict(value=round(s["T"] / mean, 1), unit="tokens/s",
+                       seconds_per_rep=round(mean, 3), reps=3,
+                       sample="the whole workload (4096 tokens): route + index permutation, fp64")
+    # decode: all 64 tokens, each routed expert's weights dequantised when used
+    if dec_res is not None:
+        spec, inp = dec_res["spec"], dec_res["inp"]
+        n = spec["T"]
+        host = {k: inp[k][:n].cpu() for k in ("x",)}
+        xs = dec(_bits(host["x"]))
+        gam = dec(_bits(inp["gamma"]))
+        w_r = dec(_bits(inp["w_r"]))
+        b = inp["bias"].cpu().double().numpy()
+
+        def weights(e):
+            def dq(key):
+                q = inp[key][e].cpu().contiguous().view(torch.uint8).numpy()
+                sc = inp["s_" + key[2:]][e].cpu().double().numpy()
+                return oracle.dequant_block_fp8(q.T, sc.T)
+            return dq("w_gate"), dq("w_up"), dq("w_down")
+
+        t0 = time.perf_counter()
+        res = oracle.moe_ffn(xs, gam, w_r, b, weights, spec["e_begin"], spec["e_count"])
+        dt = time.perf_counter() - t0
+        out[DECODE] = dict(value=round(n / dt, 2), unit="tokens/s", seconds=round(dt, 2), reps=1,
+                           active_experts=int((res["counts"] > 0).sum()),
+                           sample=f"the whole workload ({n} tokens), fp64, incl. the block-fp8 "
+                                  "dequantisation of every routed expert's weights")
+    return out
 
 
 # ---------------------------------------------------------------------- main
@@ -402,22 +641,38 @@ def main():
             peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
                                   graph_ms_per_step=res["ms_graph"],
-                                  stages=stage_report(res["work"], res["us"], peak), **res["info"]),
-                             default=str), flush=True)
+                                  stages=full_report(res["work"], res["us"], mfma_peak=peak),
+                                  **res["info"]), default=str), flush=True)
         elif args.only == "dense":
-            print(json.dumps(run_dense(args.steps, args.warmup)), flush=True)
+            r = run_dense(args.steps, args.warmup)
+            print(json.dumps(full_report(r["work"], {"rmsnorm": r["norm_us"],
+                                                     "tp_shard_mlp": r["shard_us"]})), flush=True)
         else:
-            print(json.dumps(run_router(args.steps, args.warmup)), flush=True)
+            r = run_router(args.steps, args.warmup)
+            print(json.dumps(full_report(r["work"], {"moe_route": r["route_us"],
+                                                     "moe_permute": r["perm_us"]})), flush=True)
         return
 
-    res = run_moe(PREFILL, args.steps, args.warmup)
+    # What this GPU sustains, measured first (it also brings the clock up
+    # from idle before the timed steps).
+    attain = measure_attainable()
+    log(f"[bench] attainable: {attain['mfma_bf16_tflop_s']} TFLOP/s bf16 MFMA, "
+        f"{attain['hbm_gb_s']} GB/s HBM read")
+    # written before every flushed rep: larger than the 256 MB last-level cache
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    res = run_moe(PREFILL, args.steps, args.warmup, scratch)
     spec = res["spec"]
     T = spec["T"]
-    stages = stage_report(res["work"], res["us"])
+    stages = full_report(res["work"], res["us"], res["flushed"], attain=attain)
     dom = "grouped_gate_up"
     w_dom = res["work"][dom]
-    t_dom = res["us"][dom] * 1e-6
+    t_dom = summary(res["us"][dom])["mean"] * 1e-6
     achieved = w_dom["flops"] / t_dom / 1e12
+    gemm_us = [a + b for a, b in zip(res["us"][dom], res["us"]["grouped_down"])]
+    gemm_flops = w_dom["flops"] + res["work"]["grouped_down"]["flops"]
+    step = summary(res["us"]["step"])
+    fstep = summary(res["flushed"]["step"])
     line = {
         "metric": METRIC,
         "value": round(T / (res["ms"] * 1e-3), 1),
@@ -426,6 +681,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(res["ms"], 4),
+        # per-step times of the same timed steps (first stage mark to last)
+        "step_us_median": round(step["median"], 2),
+        "step_us_min": round(step["min"], 2),
+        # K further steps, each after an untimed 512 MB scratch write
+        "flushed_step_us_median": round(fstep["median"], 2),
+        "flushed_step_us_min": round(fstep["min"], 2),
         # the same step captured once as a HIP graph and replayed (checked bit for
         # bit against the eager step)
         "graph_ms_per_step": round(res["ms_graph"], 4),
@@ -440,6 +701,7 @@ def main():
         "roofline": {"kernel": "grouped_gate_up (bf16 MFMA grouped GEMM + SiLU*up epilogue)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "frac_attainable": round(achieved / attain["mfma_bf16_tflop_s"], 4),
                      # HBM bytes per launch from the committed rocprofv3 counters
                      # (null once the kernel source differs from the profiled one)
                      "traffic": measured_traffic("grouped_gate_up",
@@ -447,48 +709,79 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": int(w_dom["bytes"]),
                      "hbm_gb_s": round(w_dom["bytes"] / t_dom / 1e9, 1)},
+        "attainable": attain,
         "stages": stages,
         "grouped_gemm_mfma_frac": round(
-            (w_dom["flops"] + res["work"]["grouped_down"]["flops"])
-            / ((res["us"][dom] + res["us"]["grouped_down"]) * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            gemm_flops / (summary(gemm_us)["mean"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
+    dec = None
     if not args.no_extra:
-        dec = run_moe(DECODE, max(10, args.steps // 2), args.warmup)
-        dstage = stage_report(dec["work"], dec["us"])
+        ksub = max(10, args.steps // 2)
+        nn = run_moe(PREFILL, ksub, args.warmup, scratch, norm=False, graph=False)
+        line["prefill_no_rmsnorm"] = {
+            "workload": PREFILL + " without rmsnorm (router and experts on x)",
+            "tokens_per_s": round(T / (nn["ms"] * 1e-3), 1), "ms_per_step": round(nn["ms"], 4),
+            "stages": full_report(nn["work"], nn["us"], nn["flushed"], attain=attain)}
+        del nn
+        torch.cuda.empty_cache()
+        dec = run_moe(DECODE, ksub, args.warmup, scratch)
         gemm_bytes = dec["work"]["grouped_gate_up"]["bytes"] + dec["work"]["grouped_down"]["bytes"]
-        gemm_us = dec["us"]["grouped_gate_up"] + dec["us"]["grouped_down"]
+        dg_us = summary([a + b for a, b in zip(dec["us"]["grouped_gate_up"],
+                                                dec["us"]["grouped_down"])])["mean"]
         line["decode"] = {"workload": DECODE, "tokens_per_s": round(64 / (dec["ms"] * 1e-3), 1),
                           "ms_per_step": round(dec["ms"], 4),
                           "graph_ms_per_step": round(dec["ms_graph"], 4), **dec["info"],
                           "grouped_gemm_hbm_frac": round(
-                              gemm_bytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                          "stages": dstage}
-        del dec
+                              gemm_bytes / (dg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                          "grouped_gemm_hbm_frac_attainable": round(
+                              gemm_bytes / (dg_us * 1e-6) / 1e9 / attain["hbm_gb_s"], 4),
+                          "stages": full_report(dec["work"], dec["us"], dec["flushed"],
+                                                attain=attain)}
+        dec["layer"] = None  # the packed weights; the inputs stay for the oracle baseline
         torch.cuda.empty_cache()
-        dm = run_moe(DECODE_MASKED, max(10, args.steps // 2), args.warmup)
+        dm = run_moe(DECODE_MASKED, ksub, args.warmup, scratch)
         line["decode_masked"] = {
             "workload": DECODE_MASKED, "tokens_per_s": round(64 / (dm["ms"] * 1e-3), 1),
             "ms_per_step": round(dm["ms"], 4), "graph_ms_per_step": round(dm["ms_graph"], 4),
             "vs_contiguous_step": round(line["decode"]["ms_per_step"] / dm["ms"], 4),
-            "stages": stage_report(dm["work"], dm["us"])}
+            "stages": full_report(dm["work"], dm["us"], dm["flushed"], attain=attain)}
         del dm
         torch.cuda.empty_cache()
-        p8 = run_moe(PREFILL_FP8, max(10, args.steps // 2), args.warmup)
+        p8 = run_moe(PREFILL_FP8, ksub, args.warmup, scratch)
         gw = p8["work"]["grouped_gate_up"]["flops"] + p8["work"]["grouped_down"]["flops"]
-        gus = p8["us"]["grouped_gate_up"] + p8["us"]["grouped_down"]
+        gus = summary([a + b for a, b in zip(p8["us"]["grouped_gate_up"],
+                                             p8["us"]["grouped_down"])])["mean"]
         line["prefill_fp8_activations"] = {
             "workload": PREFILL_FP8, "tokens_per_s": round(T / (p8["ms"] * 1e-3), 1),
             "ms_per_step": round(p8["ms"], 4), "graph_ms_per_step": round(p8["ms_graph"], 4),
+            "vs_bf16_step": round(res["ms"] / p8["ms"], 4),
             **p8["info"],
             # the GEMM stages include the activation quantisation that feeds them
             "grouped_gemm_fp8_mfma_frac": round(gw / (gus * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
-            "stages": stage_report(p8["work"], p8["us"], PEAK_FP8_TFLOPS)}
+            "stages": full_report(p8["work"], p8["us"], p8["flushed"], PEAK_FP8_TFLOPS,
+                                  attain=attain)}
         del p8
         torch.cuda.empty_cache()
-        line["dense_shard"] = run_dense(max(10, args.steps // 2), args.warmup)
-        line["router_only"] = run_router(max(10, args.steps // 2), args.warmup)
+        dn = run_dense(ksub, args.warmup, scratch)
+        line["dense_shard"] = {
+            "workload": DENSE,
+            "stages": full_report(dn["work"], {"rmsnorm": dn["norm_us"],
+                                               "tp_shard_mlp": dn["shard_us"]},
+                                  {"rmsnorm": dn["flushed"][0], "tp_shard_mlp": dn["flushed"][1]},
+                                  attain=attain)}
+        rt = run_router(ksub, args.warmup, scratch)
+        line["router_only"] = {
+            "workload": ROUTER,
+            "stages": full_report(rt["work"], {"moe_route": rt["route_us"],
+                                               "moe_permute": rt["perm_us"]},
+                                  {"moe_route": rt["flushed"][0], "moe_permute": rt["flushed"][1]},
+                                  attain=attain)}
+        line["dense_f32"] = run_dense_f32(ksub, args.warmup)
+    del scratch
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res)
+        line["cpu_baselines"] = cpu_baselines_other(dec)
     print(json.dumps(line), flush=True)
 
 

@@ -53,6 +53,8 @@ _SIGNATURES = {
                                   _c_void_p, _c_void_p]),
     "grouped_down_a8": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32,
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "mf_probe_mfma_bf16": (_i32, [_i32, _i32, _c_void_p, _c_void_p]),
+    "mf_probe_hbm_read": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p]),
     "tp_shard_mlp": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
                             _c_void_p, _c_void_p, _c_void_p]),
 }

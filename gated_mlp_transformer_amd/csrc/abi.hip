@@ -44,7 +44,7 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d, flo
             int32_t dtype, void* stream) {
   if (T < 0 || d <= 0 || !(eps >= 0.f) || !isfinite(eps)) return MF_EINVAL;
   if (dtype != MF_BF16 && dtype != MF_F32) return MF_EINVAL;
-  if (d % 64 != 0 || d > (dtype == MF_BF16 ? 8192 : 4096)) return MF_EUNSUPPORTED;
+  if (d % 64 != 0 || d > 8192) return MF_EUNSUPPORTED;
   if (T == 0) return MF_OK;  // zero-size buffers may be NULL
   if (!x || !gamma || !y) return MF_EINVAL;
   if (!a16(x) || !a16(gamma) || !a16(y)) return MF_EUNSUPPORTED;
@@ -369,6 +369,20 @@ int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s, const 
                          static_cast<const float*>(w_up_s), static_cast<const float*>(w_down_s),
                          T, d, f_s, static_cast<float*>(h_work), partial, s);
   }
+  return finish();
+}
+
+int mf_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, void* stream) {
+  if (workgroups < 1 || iters < 1 || !out) return MF_EINVAL;
+  mf::launch_probe_mfma(workgroups, iters, out, S(stream));
+  return finish();
+}
+
+int mf_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                      void* stream) {
+  if (!src || !out || bytes < 16 || bytes % 16 != 0 || workgroups < 1) return MF_EINVAL;
+  if (!a16(src)) return MF_EUNSUPPORTED;
+  mf::launch_probe_read(src, bytes, workgroups, out, S(stream));
   return finish();
 }
 

@@ -6,6 +6,10 @@
 // ("推理计算流梳理", Norm&Residual: the layer output is the residual stream plus
 // the FFN of its normalised copy), added after the weighted sum.
 //
+// out may be the residual buffer itself: each element of the residual is read
+// by the thread that then writes the same element of out, so neither pointer
+// is declared restrict.
+//
 // A gather, not a scatter: one 256-thread workgroup per token reads at most k
 // rows of y_perm with 16-byte loads and sums them in fp32 in slot order, so the
 // result is deterministic and needs no atomics. HBM-bound: the bytes are the k
@@ -19,8 +23,8 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const bf16_t* __restrict__ y,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ w, int k, int d,
-                                                      int64_t max_rows, const void* __restrict__ residual,
-                                                      void* __restrict__ out) {
+                                                      int64_t max_rows, const void* residual,
+                                                      void* out) {
   const int64_t t = blockIdx.x;
   int64_t pos[8];
   float wt[8];

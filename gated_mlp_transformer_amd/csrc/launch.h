@@ -86,4 +86,9 @@ void launch_dense_f32(const float* x, const float* w_gate, const float* w_up,
                       const float* w_down, int64_t T, int d, int fs, float* h,
                       float* partial, hipStream_t s);
 
+// Measurement probes (probe.hip): out has workgroups * 256 elements.
+void launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t s);
+void launch_probe_read(const void* src, int64_t bytes, int workgroups, uint32_t* out,
+                       hipStream_t s);
+
 }  // namespace mf

@@ -172,6 +172,12 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
     case 4: rmsnorm_full_kernel<T, 4><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
     case 8: rmsnorm_full_kernel<T, 8><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
     case 16: rmsnorm_full_kernel<T, 16><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 32:  // f32 rows of 8192
+      if constexpr (sizeof(T) == 4) {
+        rmsnorm_full_kernel<T, 32><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps);
+        return true;
+      }
+      return false;
     default: return false;
   }
 }
@@ -188,7 +194,7 @@ void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
   if (blocks > 2048) blocks = 2048;
   const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : blocks));
   // registers for one row per lane: 8 x 16 bytes cover d <= 4096 (bf16) /
-  // 2048 (f32); 16 cover the largest rows the ABI accepts
+  // 2048 (f32); 16 cover bf16 rows up to 8192 and 32 the f32 ones
   const bool small = d * (bf16 ? 2 : 4) <= 8 * 16 * kWave;
   if (bf16) {
     auto* xp = static_cast<const bf16_t*>(x);
@@ -201,7 +207,8 @@ void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
     auto* gp = static_cast<const float*>(gamma);
     auto* yp = static_cast<float*>(y);
     if (small) rmsnorm_kernel<float, 8><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
-    else rmsnorm_kernel<float, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
+    else if (d * 4 <= 16 * 16 * kWave) rmsnorm_kernel<float, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
+    else rmsnorm_kernel<float, 32><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
   }
 }
 

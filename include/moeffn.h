@@ -67,7 +67,7 @@ const char* mf_version(void);
  * x, y   [T, d]  dtype (MF_BF16 or MF_F32); y may alias x.
  * gamma  [d]     dtype.
  * Math in fp32; y is rounded to nearest-even into dtype.
- * Requires d % 64 == 0 and d <= 8192 (bf16) / d <= 4096 (f32); eps >= 0.
+ * Requires d % 64 == 0 and d <= 8192; eps >= 0 (MF_EUNSUPPORTED beyond 8192).
  */
 int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
             float eps, int32_t dtype, void* stream);
@@ -374,6 +374,26 @@ int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
 int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s,
                  const void* w_down_s, int64_t T, int32_t d, int32_t f_s,
                  int32_t dtype, void* h_work, float* partial, void* stream);
+
+/*
+ * Measurement probes. Not part of the FFN path: they state what this GPU
+ * sustains, so that a benchmark can report its kernels' fractions of the
+ * attainable rates beside the published peaks.
+ *
+ * mf_probe_mfma_bf16 - `workgroups` workgroups of four waves; every wave
+ *   issues iters * 16 back-to-back v_mfma_f32_32x32x16_bf16 on 16 independent
+ *   accumulators (no memory traffic in the loop). FLOPs =
+ *   workgroups * 4 * iters * 16 * 32768. out [workgroups * 256] f32 receives
+ *   one folded value per thread.
+ * mf_probe_hbm_read - reads bytes (a multiple of 16) of src once, with
+ *   grid-strided 16-byte loads from `workgroups` 256-thread workgroups; out
+ *   [workgroups * 256] u32 receives one folded word per thread.
+ * Both are asynchronous on `stream`; time them with events. MF_EINVAL on bad
+ * arguments.
+ */
+int mf_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, void* stream);
+int mf_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -76,7 +76,11 @@ def dequant_block_fp8(q_bits, scales, block: int = 128) -> np.ndarray:
     rows, cols = q.shape
     assert rows % block == 0 and cols % block == 0
     assert s.shape == (rows // block, cols // block)
-    return q * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    # element (i, j) sits in block (i // block, j // block): view q as
+    # [row block, row in block, column block, column in block] and multiply
+    # each element by its block's scale
+    qb = q.reshape(rows // block, block, cols // block, block)
+    return (qb * s[:, None, :, None]).reshape(rows, cols)
 
 
 # ---------------------------------------------------------------------------

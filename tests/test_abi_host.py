@@ -64,7 +64,7 @@ def test_rmsnorm_validation(lib):
     assert lib.rmsnorm(P, P, P, 4, 64, 1e-5, 7, N) == MF_EINVAL
     assert lib.rmsnorm(P, P, P, 4, 96, 1e-5, BF16, N) == MF_EUNSUPPORTED
     assert lib.rmsnorm(P, P, P, 4, 8256, 1e-5, BF16, N) == MF_EUNSUPPORTED
-    assert lib.rmsnorm(P, P, P, 4, 8192, 1e-5, F32, N) == MF_EUNSUPPORTED
+    assert lib.rmsnorm(P, P, P, 4, 8256, 1e-5, F32, N) == MF_EUNSUPPORTED
     assert lib.rmsnorm(ctypes.c_void_p(0x100008), P, P, 4, 64, 1e-5, BF16, N) == MF_EUNSUPPORTED
     assert lib.rmsnorm(P, P, P, 0, 64, 1e-5, BF16, N) == MF_OK
 

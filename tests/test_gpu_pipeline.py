@@ -17,8 +17,10 @@ raw inputs:
   * end to end: the oracle's fp64 sub-block from the raw x with the routed
     sets the GPU chose (accepted above): tolerance on the output.
 
-At full sizes the floating-point stages are checked on sampled rows or
-columns the oracle computes one by one (tokens and columns are independent).
+Every size is checked in full: every token, every row of H and Y_perm and
+every column. The oracle's end-to-end pass visits each local expert once, and
+the stage references of that expert's rows are computed from the same fp64
+weights in that visit.
 """
 
 import numpy as np
@@ -56,40 +58,34 @@ def expert_f64(inp, e, wdtype):
             fp8_weight_f64(inp["w_down"][e], inp["s_down"][e]))
 
 
-def weight_rows_f64(inp, key, e, rows, wdtype):
-    """Rows `rows` of expert e's [out, in] weight `key`, fp64 (fp8: dequantised)."""
-    if wdtype == "bf16":
-        return to_f64(inp[key][e][rows])
-    out = []
-    for r in rows:  # dequantise the 128-row block holding each row (cached per block)
-        b = r // 128
-        if not out or out[-1][0] != b:
-            q = inp[key][e][b * 128:(b + 1) * 128]
-            s = inp["s_" + key[2:]][e][b:b + 1]
-            out.append((b, fp8_weight_f64(q, s).T, []))  # block as [128, K]
-        out[-1][2].append(out[-1][1][r - b * 128])
-    return np.stack([row for _, _, rs in out for row in rs])
-
-
-def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
-                col_sample=None, e2e_tokens=None):
-    """Stage-by-stage and end-to-end parity of one forward pass (see module doc).
+def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, masked=None):
+    """Stage-by-stage and end-to-end parity of one forward pass (see module doc),
+    on every token, row and column.
 
     With the layer's fp8 activations (block-fp8 prefill variant) the GEMMs are
     checked on the GPU's own codes: gate/up on the quantised V rows it
     gathers, down on the quantised H (whose codes are compared bit for bit
     with the oracle's quantiser on the GPU's H); end to end against the
-    oracle's fp8-activation sub-block."""
+    oracle's fp8-activation sub-block. A layer without gamma runs the router
+    on x itself (no RMSNorm), and so does the oracle. ``masked``, a twin layer
+    with the masked (fixed-capacity) layout on the same inputs, is checked
+    against the same oracle values: its dispatch integers, its H and Y rows at
+    the slots' block rows, and its output."""
     a8 = getattr(layer, "act_fp8", False)
+    norm = layer.gamma is not None
     rel = 5e-3 if wdtype == "bf16" else REL_FP8
     out = layer(inp["x"])
+    out_m = masked(inp["x"]) if masked is not None else None
     torch.cuda.synchronize()
     x = to_f64(inp["x"])
-    rows = np.arange(T) if token_sample is None else np.asarray(token_sample)
+    gamma = to_f64(inp["gamma"]) if norm else None
 
     # RMSNorm
-    v_gpu = to_f64(layer.v)
-    assert_fp("V", v_gpu[rows], oracle.rmsnorm(x[rows], to_f64(inp["gamma"]), 1e-5))
+    if norm:
+        v_gpu = to_f64(layer.v)
+        assert_fp("V", v_gpu, oracle.rmsnorm(x, gamma, 1e-5))
+    else:
+        v_gpu = x
 
     # router on the GPU's V
     w_r, bias = to_f64(inp["w_r"]), to_f64(inp["bias"])
@@ -108,8 +104,8 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
     assert np.array_equal(to_i64(layer.src_token)[:S], src)
     assert np.array_equal(to_i64(layer.inv_pos), inv)
 
-    # expert GEMMs on the gathered rows V[src_token] (H) and the GPU's H
-    # (Y_perm): all rows, sampled columns
+    # the GEMMs' own inputs: the rows V[src_token] the gate/up GEMM gathers,
+    # and the GPU's H for the down GEMM
     if a8:
         vq = layer.vq.cpu().numpy().astype(np.uint8)
         xp = oracle.dequant_rows(vq[src], layer.vs.double().cpu().numpy()[src])
@@ -122,37 +118,56 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, token_sample=None,
         xp = v_gpu[src]
         h_in = to_f64(layer.h[:S])
         rel_gemm = rel
+    h_ref = np.zeros((S, f))
+    y_ref = np.zeros((S, d))
+
+    def weights(e):
+        # The oracle's end-to-end pass asks for each local expert that holds
+        # rows once, in ascending order; the stage references of that expert's
+        # rows are computed here from the same fp64 weights.
+        wg, wu, wd = expert_f64(inp, e, wdtype)
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        h_ref[a:b] = oracle.silu(xp[a:b] @ wg) * (xp[a:b] @ wu)
+        y_ref[a:b] = h_in[a:b] @ wd
+        return wg, wu, wd
+
+    # end to end from the raw inputs, with the GPU's accepted routed sets
+    ref = oracle.moe_ffn(x, gamma, w_r, bias, weights, eb, ec, idx=gpu_idx, act_fp8=a8,
+                         norm=norm)
+    assert np.array_equal(ref["offsets"], offsets)
     h_gpu = to_f64(layer.h[:S])
     y_gpu = to_f64(layer.y_perm[:S])
-    hc = np.arange(f) if col_sample is None else np.asarray(col_sample)
-    yc = np.arange(d) if col_sample is None else np.asarray(col_sample)
-    h_ref = np.zeros((S, len(hc)))
-    y_ref = np.zeros((S, len(yc)))
-    for e in range(ec):
-        a, b = offsets[e], offsets[e + 1]
-        if b == a:
-            continue
-        wg = weight_rows_f64(inp, "w_gate", e, list(hc), wdtype)
-        wu = weight_rows_f64(inp, "w_up", e, list(hc), wdtype)
-        wd = weight_rows_f64(inp, "w_down", e, list(yc), wdtype)
-        h_ref[a:b] = oracle.silu(xp[a:b] @ wg.T) * (xp[a:b] @ wu.T)
-        y_ref[a:b] = h_in[a:b] @ wd.T
-    assert_fp("H", h_gpu[:, hc], h_ref, rel=rel_gemm, max_abs=None)
-    assert_fp("Y_perm (from GPU H)", y_gpu[:, yc], y_ref, rel=rel_gemm, max_abs=None)
+    assert_fp("H", h_gpu, h_ref, rel=rel_gemm, max_abs=None)
+    assert_fp("Y_perm (from GPU H)", y_gpu, y_ref, rel=rel_gemm, max_abs=None)
 
     # combine on the GPU's Y_perm
     out_gpu = to_f64(out)
-    comb = oracle.combine(to_f64(layer.y_perm), inv[rows], to_f64(layer.topk_w)[rows])
-    assert_fp("combine", out_gpu[rows], comb)
+    comb = oracle.combine(to_f64(layer.y_perm), inv, to_f64(layer.topk_w))
+    assert_fp("combine", out_gpu, comb)
 
-    # end to end from the raw inputs, with the GPU's accepted routed sets
-    et = rows if e2e_tokens is None else np.asarray(e2e_tokens)
-    need = sorted({int(i) - eb for t in et for i in gpu_idx[t] if eb <= i < eb + ec})
-    cache = {e: expert_f64(inp, e, wdtype) for e in need}
-    ref = oracle.moe_ffn(x[et], to_f64(inp["gamma"]), w_r, bias,
-                         lambda e: cache[e], eb, ec, idx=gpu_idx[et], act_fp8=a8)
     max_abs = 2e-2 if wdtype == "bf16" else None
-    assert_fp("FFN output (end to end)", out_gpu[et], ref["out"], rel=rel, max_abs=max_abs)
+    assert_fp("FFN output (end to end)", out_gpu, ref["out"], rel=rel, max_abs=max_abs)
+
+    if masked is not None:
+        cap = masked.cap
+        m_counts, m_rows, m_pos = oracle.dispatch_masked(to_i64(masked.idx), eb, ec, cap)
+        assert np.array_equal(to_i64(masked.idx), gpu_idx)
+        assert np.array_equal(to_i64(masked.counts), m_counts)
+        assert np.array_equal(to_i64(masked.inv_pos), m_pos)
+        used = m_rows >= 0
+        assert np.array_equal(to_i64(masked.row_index)[used], m_rows[used])
+        local = inv >= 0
+        assert np.array_equal(m_pos >= 0, local)  # cap >= T: no slot dropped
+        # slot (t, j) lives at contiguous row inv[t, j] and masked row m_pos[t, j]
+        hm = to_f64(masked.h)[m_pos[local]]
+        ym = to_f64(masked.y_perm)[m_pos[local]]
+        assert_fp("masked H", hm, h_ref[inv[local]], rel=rel_gemm, max_abs=None)
+        # its H rows are the contiguous layer's (same rows, same kernels), so
+        # y_ref (computed from the contiguous H) is its down GEMM's reference
+        assert np.array_equal(hm, h_gpu[inv[local]])
+        assert_fp("masked Y (from its H)", ym, y_ref[inv[local]], rel=rel_gemm, max_abs=None)
+        assert_fp("masked FFN output (end to end)", to_f64(out_m), ref["out"], rel=rel,
+                  max_abs=max_abs)
     return dict(S=S, near_ties=n_near)
 
 
@@ -206,21 +221,21 @@ def test_workload_router_4096tok(g):
 
 
 def test_workload_dense_shard_4096(g):
-    """RMSNorm + one bf16 TP shard (4096 x 4096, f_s 2048): sampled rows."""
+    """RMSNorm + one bf16 TP shard (4096 x 4096, f_s 2048): every row and column."""
     spec = WORKLOADS["norm_tp_shard_bf16_4096"]
     T, d, f = spec["T"], spec["d"], spec["f"]
     D = make_dense(T, d, f, dtype=torch.bfloat16, norm=True, device=DEV)
     v = g.rmsnorm(D["x"], D["gamma"], 1e-5)
     part, h = g.tp_shard_mlp(v, *(g.pack_weights(D[k]) for k in ("w_gate", "w_up", "w_down")))
     torch.cuda.synchronize()
-    rows = np.random.default_rng(0).choice(T, size=192, replace=False)
-    rows[:2] = [0, T - 1]
-    x = to_f64(D["x"])[rows]
-    assert_fp("V", to_f64(v)[rows], oracle.rmsnorm(x, to_f64(D["gamma"]), 1e-5))
-    vg = to_f64(v)[rows]
+    x = to_f64(D["x"])
+    assert_fp("V", to_f64(v), oracle.rmsnorm(x, to_f64(D["gamma"]), 1e-5))
+    vg = to_f64(v)
     wg, wu, wd = (to_f64(D[k]).T for k in ("w_gate", "w_up", "w_down"))
-    assert_fp("H", to_f64(h)[rows], oracle.silu(vg @ wg) * (vg @ wu), max_abs=None)
-    assert_fp("partial", to_f64(part)[rows], oracle.tp_shard_mlp(vg, wg, wu, wd, 1, 0))
+    assert_fp("H", to_f64(h), oracle.silu(vg @ wg) * (vg @ wu), max_abs=None)
+    # the down GEMM on the GPU's H, then the shard end to end from the GPU's V
+    assert_fp("partial (from GPU H)", to_f64(part), to_f64(h) @ wd, max_abs=None)
+    assert_fp("partial", to_f64(part), oracle.tp_shard_mlp(vg, wg, wu, wd, 1, 0))
 
 
 @pytest.fixture(scope="module")
@@ -233,19 +248,27 @@ def prefill(g):
 
 
 def test_workload_prefill_8192tok(g, prefill):
+    """The prefill workload in full: every token, row and column."""
     spec, inp, layer = prefill
-    T = spec["T"]
-    r = np.random.default_rng(1)
-    tokens = np.sort(r.choice(T, size=256, replace=False))
-    tokens[0], tokens[-1] = 0, T - 1
-    res = check_layer(g, layer, inp, T, spec["d"], spec["f"], spec["E"], spec["e_begin"],
-                      spec["e_count"], "bf16", token_sample=tokens,
-                      col_sample=list(range(96, 128)) + [2047],
-                      e2e_tokens=tokens[:12])
+    res = check_layer(g, layer, inp, spec["T"], spec["d"], spec["f"], spec["E"],
+                      spec["e_begin"], spec["e_count"], "bf16")
     counts = to_i64(layer.counts)
     # the skewed bias gives the local experts uneven loads (0.5x to 3x the mean)
     assert counts.max() > 2 * counts.mean() and counts.min() > 0
     assert res["S"] == counts.sum()
+
+
+def test_workload_prefill_8192tok_without_rmsnorm(g, prefill):
+    """The same workload with the router and experts fed x directly (no
+    RMSNorm stage): the sub-block as the workload list states it."""
+    spec, inp, _ = prefill
+    no_norm = dict(inp)
+    no_norm["gamma"] = None
+    layer = build_layer(g, no_norm, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    assert layer.v is None
+    res = check_layer(g, layer, no_norm, spec["T"], spec["d"], spec["f"], spec["E"],
+                      spec["e_begin"], spec["e_count"], "bf16")
+    assert res["S"] == to_i64(layer.counts).sum()
 
 
 def test_prefill_is_deterministic(g, prefill):
@@ -256,32 +279,6 @@ def test_prefill_is_deterministic(g, prefill):
     assert torch.equal(a, b)
 
 
-def test_workload_decode_64tok_fp8(g):
-    spec = WORKLOADS["moe_decode_64tok_256exp_fp8"]
-    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
-                   wdtype="fp8", device=DEV)
-    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
-    res = check_layer(g, layer, inp, spec["T"], spec["d"], spec["f"], spec["E"],
-                      spec["e_begin"], spec["e_count"], "fp8",
-                      col_sample=list(range(256, 288)), e2e_tokens=[0, 63])
-    assert res["S"] == 64 * 8
-
-
-def test_workload_prefill_8192tok_fp8_activations(g):
-    spec = WORKLOADS["moe_prefill_8192tok_32exp_fp8act"]
-    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
-                   wdtype="fp8", zipf=spec["zipf"], device=DEV)
-    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"], act_fp8=True)
-    T = spec["T"]
-    r = np.random.default_rng(2)
-    tokens = np.sort(r.choice(T, size=128, replace=False))
-    tokens[0], tokens[-1] = 0, T - 1
-    res = check_layer(g, layer, inp, T, spec["d"], spec["f"], spec["E"], spec["e_begin"],
-                      spec["e_count"], "fp8", token_sample=tokens,
-                      col_sample=list(range(128, 160)) + [2047], e2e_tokens=tokens[:6])
-    assert res["S"] == to_i64(layer.counts).sum()
-
-
 def _masked_twin(g, inp, T, d, f, eb, cap=None):
     return g.MoEFFNLayer(T=T, d=d, f=f, w_r=inp["w_r"], bias=inp["bias"], gamma=inp.get("gamma"),
                          w_gate=inp["w_gate"], w_up=inp["w_up"], w_down=inp["w_down"],
@@ -289,36 +286,42 @@ def _masked_twin(g, inp, T, d, f, eb, cap=None):
                          s_down=inp.get("s_down"), layout="masked", cap=cap)
 
 
-@pytest.mark.parametrize("wdtype,T,eb,ec", [("bf16", 200, 16, 16), ("fp8", 64, 0, 64)])
-def test_masked_layout_equals_contiguous(g, wdtype, T, eb, ec):
-    """The masked (fixed-capacity) layout changes where rows live, not their
-    arithmetic: the layer output is bit-identical to the contiguous layer's,
-    which check_layer ties to the oracle; the dispatch integers are the
-    oracle's."""
-    d, f, E = 256, 256, 64
-    inp = make_moe(T, d, f, E, eb, ec, wdtype=wdtype, seed=T + ec + 9, device=DEV)
-    contig = build_layer(g, inp, T, d, f, eb)
-    check_layer(g, contig, inp, T, d, f, E, eb, ec, wdtype)
-    masked = _masked_twin(g, inp, T, d, f, eb)
-    a = contig(inp["x"]).clone()
-    b = masked(inp["x"]).clone()
-    torch.cuda.synchronize()
-    counts, rows, pos = oracle.dispatch_masked(to_i64(masked.idx), eb, ec, T)
-    assert np.array_equal(to_i64(masked.counts), counts)
-    assert np.array_equal(to_i64(masked.inv_pos), pos)
-    used = rows >= 0
-    assert np.array_equal(to_i64(masked.row_index)[used], rows[used])
-    assert torch.equal(a, b)
-
-
-def test_workload_decode_64tok_fp8_masked(g):
+def test_workload_decode_64tok_fp8(g):
+    """The decode workload in full (all 64 tokens, every row and column), in
+    the contiguous layout and in the masked layout, each against the oracle."""
     spec = WORKLOADS["moe_decode_64tok_256exp_fp8"]
     inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
                    wdtype="fp8", device=DEV)
-    contig = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
     masked = _masked_twin(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    res = check_layer(g, layer, inp, spec["T"], spec["d"], spec["f"], spec["E"],
+                      spec["e_begin"], spec["e_count"], "fp8", masked=masked)
+    assert res["S"] == 64 * 8
+    assert int(masked.counts.sum()) == spec["T"] * 8
+
+
+def test_workload_prefill_8192tok_fp8_activations(g):
+    """The block-fp8 prefill variant in full: every token, row and column."""
+    spec = WORKLOADS["moe_prefill_8192tok_32exp_fp8act"]
+    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
+                   wdtype="fp8", zipf=spec["zipf"], device=DEV)
+    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"], act_fp8=True)
+    res = check_layer(g, layer, inp, spec["T"], spec["d"], spec["f"], spec["E"],
+                      spec["e_begin"], spec["e_count"], "fp8")
+    assert res["S"] == to_i64(layer.counts).sum()
+
+
+@pytest.mark.parametrize("wdtype,T,eb,ec", [("bf16", 200, 16, 16), ("fp8", 64, 0, 64)])
+def test_masked_layout_equals_contiguous(g, wdtype, T, eb, ec):
+    """The masked (fixed-capacity) layout changes where rows live, not their
+    arithmetic: both layers are checked against the oracle, and the masked
+    output is bit-identical to the contiguous one."""
+    d, f, E = 256, 256, 64
+    inp = make_moe(T, d, f, E, eb, ec, wdtype=wdtype, seed=T + ec + 9, device=DEV)
+    contig = build_layer(g, inp, T, d, f, eb)
+    masked = _masked_twin(g, inp, T, d, f, eb)
+    check_layer(g, contig, inp, T, d, f, E, eb, ec, wdtype, masked=masked)
     a = contig(inp["x"]).clone()
     b = masked(inp["x"]).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    assert int(masked.counts.sum()) == spec["T"] * 8

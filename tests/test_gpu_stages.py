@@ -36,10 +36,8 @@ def routing_ids(T, E, k, seed):
 # ------------------------------------------------------------------ rmsnorm --
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("T,d", [(1, 64), (37, 256), (300, 4096), (5, 8192)])
+@pytest.mark.parametrize("T,d", [(1, 64), (37, 256), (300, 4096), (5, 8192), (9, 6208)])
 def test_rmsnorm(g, dtype, T, d):
-    if dtype == torch.float32 and d > 4096:
-        pytest.skip("fp32 rows are limited to d <= 4096")
     x = synth.normal((T, d), name="t.rms.x", sub=d, dtype=dtype, device=DEV)
     if T > 2:
         x[0] = 0
@@ -50,6 +48,15 @@ def test_rmsnorm(g, dtype, T, d):
     ref = oracle.rmsnorm(to_f64(x), to_f64(gamma), 1e-5)
     tol = dict(rel=5e-3, max_abs=2e-2) if dtype == torch.bfloat16 else dict(rel=1e-6, max_abs=1e-5)
     assert_fp("rmsnorm", to_f64(y), ref, **tol)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rmsnorm_rows_beyond_8192_are_unsupported(g, dtype):
+    x = torch.zeros((2, 8256), dtype=dtype, device=DEV)
+    gamma = torch.ones(8256, dtype=dtype, device=DEV)
+    with pytest.raises(g.MoEFFNError) as e:
+        g.rmsnorm(x, gamma, 1e-5)
+    assert e.value.status == -2  # MF_EUNSUPPORTED, nothing enqueued
 
 
 def test_rmsnorm_in_place(g):
@@ -382,6 +389,29 @@ def test_combine(g, out_dtype, with_residual):
     assert np.all(got[none_local] == (0 if r is None else to_f64(r)[none_local]))
     tol = dict(rel=5e-3, max_abs=2e-2) if out_dtype == torch.bfloat16 else dict(rel=1e-6, max_abs=1e-5)
     assert_fp("combine", got, ref, **tol)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_combine_out_aliases_residual(g, out_dtype):
+    """out may be the residual buffer itself (the residual stream updated in
+    place): the result equals the combine into a separate buffer, bit for bit."""
+    T, E, k, d = 300, 64, 8, 256
+    idx = routing_ids(T, E, k, seed=12)
+    res = g.moe_permute(idx, 0, 40, None)
+    y_perm = synth.normal((T * k, d), name="t.comb.alias.y", device=DEV)
+    w = torch.rand((T, k), generator=torch.Generator(DEV).manual_seed(4), device=DEV) + 0.05
+    w = (w / w.sum(1, keepdim=True)).float().contiguous()
+    r = synth.normal((T, d), name="t.comb.alias.r", dtype=out_dtype, device=DEV)
+    sep = g.moe_combine(y_perm, res.inv_pos, w, out_dtype=out_dtype, residual=r)
+    stream_buf = r.clone()
+    same = g.moe_combine(y_perm, res.inv_pos, w, out_dtype=out_dtype, residual=stream_buf,
+                         out=stream_buf)
+    torch.cuda.synchronize()
+    assert same.data_ptr() == stream_buf.data_ptr()
+    assert torch.equal(sep, stream_buf)
+    ref = oracle.combine(to_f64(y_perm), to_i64(res.inv_pos), to_f64(w), residual=to_f64(r))
+    tol = dict(rel=5e-3, max_abs=2e-2) if out_dtype == torch.bfloat16 else dict(rel=1e-6, max_abs=1e-5)
+    assert_fp("combine in place", to_f64(stream_buf), ref, **tol)
 
 
 # ------------------------------------------------------------- TP shards --

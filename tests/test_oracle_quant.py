@@ -154,3 +154,59 @@ def test_experts_a8_runs_each_expert_on_its_rows():
         if b > a:
             ye, he = oracle.swiglu_a8(x[a:b], *W[e])
             assert np.array_equal(y[a:b], ye) and np.array_equal(h[a:b], he)
+
+
+def _torch_quantize_rows(x64: np.ndarray) -> np.ndarray:
+    """Per-token 1x128 fp8 activations written with torch's own float32
+    arithmetic and float8_e4m3fn cast (not the oracle's encoder): returns the
+    dequantised values code * scale."""
+    x = torch.from_numpy(x64).float()
+    rows, K = x.shape
+    g = x.reshape(rows, K // 128, 128)
+    s = torch.clamp(g.abs().amax(dim=2), min=1e-4) / 448.0
+    q = (g / s[:, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return (q.double() * s.double()[:, :, None]).reshape(rows, K).numpy()
+
+
+def _bf16(x64: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(x64)).float().bfloat16().double().numpy()
+
+
+def test_moe_ffn_fp8_activations_matches_per_token_definition():
+    # The block-fp8 prefill sub-block, token by token from its definition:
+    # v = bf16(RMSNorm(x)); routed set and weights from v; for each local
+    # expert e in the set: h = bf16(SiLU(Q(v) Wg_e) * (Q(v) Wu_e)) and
+    # y = Q(h) Wd_e with Q the per-token 1x128 fp8 quantise-dequantise;
+    # out = sum over local e of w_e * y_e. Torch ops throughout (rms_norm,
+    # float32 division, the float8_e4m3fn and bfloat16 casts), so a wiring slip
+    # in the oracle's permute -> experts_a8 -> combine path (a dropped bf16
+    # rounding of V, the unquantised V in one product, a wrong expert's
+    # weights, a mis-scaled combine) shows up here.
+    import torch.nn.functional as F
+    r = rng(46)
+    T, d, f, E, eb, ec = 19, 256, 128, 12, 2, 7
+    x = r.standard_normal((T, d))
+    gam = 1 + 0.1 * r.standard_normal(d)
+    w_r, b = r.standard_normal((E, d)) * 0.05, r.standard_normal(E) * 0.05
+    ws = [tuple(r.normal(0, 0.05, s) for s in ((d, f), (d, f), (f, d))) for _ in range(ec)]
+    res = oracle.moe_ffn(x, gam, w_r, b, ws, eb, ec, act_fp8=True)
+    v = F.rms_norm(torch.from_numpy(x), (d,), weight=torch.from_numpy(gam), eps=1e-5).numpy()
+    vb = _bf16(v)
+    for t in range(T):
+        # routing is the same as the bf16 path's (on v, not on its bf16 copy)
+        z = v[t] @ w_r.T
+        s = 1 / (1 + np.exp(-z))
+        top = np.sort(np.lexsort((np.arange(E), -(s + b)))[:8])
+        assert np.array_equal(res["idx"][t], top)
+        acc = np.zeros(d)
+        xq = _torch_quantize_rows(vb[t:t + 1])
+        for e in top:
+            if eb <= e < eb + ec:
+                wg, wu, wd = ws[e - eb]
+                h = _bf16(F.silu(torch.from_numpy(xq @ wg)).numpy() * (xq @ wu))
+                acc += s[e] / s[top].sum() * (_torch_quantize_rows(h) @ wd)[0]
+        assert np.allclose(res["out"][t], acc, rtol=1e-10, atol=1e-12), t
+    # some tokens have no local expert (exact zeros), most have several
+    n_local = np.isin(res["idx"], np.arange(eb, eb + ec)).sum(1)
+    assert np.all(res["out"][n_local == 0] == 0)
+    assert n_local.max() >= 3
