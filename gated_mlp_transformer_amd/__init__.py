@@ -29,7 +29,7 @@ _lib.load()  # fail loudly at import if the HIP library is missing
 __all__ = [
     "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "moe_route_workspace_size",
     "moe_route",
-    "moe_permute_workspace_size", "moe_permute", "moe_dispatch_masked", "MaskedDispatch",
+    "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc", "moe_dispatch_masked", "MaskedDispatch",
     "grouped_gate_up_masked", "grouped_down_masked", "quantize_fp8_rows", "grouped_gate_up_a8",
     "grouped_down_a8",
     "grouped_swiglu", "grouped_gate_up", "grouped_down", "moe_combine", "tp_shard_mlp", "PermuteResult", "MoEFFNLayer",
@@ -225,6 +225,38 @@ def moe_permute(topk_idx: torch.Tensor, e_begin: int, e_count: int,
         _p(topk_idx), T, k, e_begin, e_count, _p(x), d, xdt, _p(x_perm), _p(counts),
         _p(offsets), _p(src_token), _p(inv_pos), _p(workspace),
         workspace.numel() * workspace.element_size(), _s(stream)))
+    return PermuteResult(counts, offsets, src_token, inv_pos, x_perm)
+
+
+def moe_permute_noalloc(topk_idx: torch.Tensor, e_begin: int, e_count: int,
+                        x: Optional[torch.Tensor] = None, *, x_perm: torch.Tensor,
+                        counts: torch.Tensor, offsets: torch.Tensor, src_token: torch.Tensor,
+                        inv_pos: torch.Tensor, stream=None) -> PermuteResult:
+    """moe_permute through the allocation-free entry point: every output buffer
+    is the caller's (nothing is allocated here or in the library; the count
+    tables live in the library's static device array). ``x_perm`` may be None
+    only when ``x`` is None (indices only)."""
+    T, k = topk_idx.shape
+    i32 = torch.int32
+    if topk_idx.dtype != i32:
+        raise ValueError("moe_permute_noalloc: topk_idx must be int32")
+    for what, t, shape in (("counts", counts, (e_count,)), ("offsets", offsets, (e_count + 1,)),
+                           ("src_token", src_token, (T * k,)), ("inv_pos", inv_pos, (T, k))):
+        if t is None:
+            raise ValueError(f"moe_permute_noalloc: {what} is required")
+        _need("moe_permute_noalloc", what, t, shape, i32)
+    d, xdt = 0, MF_BF16
+    if x is not None:
+        d = x.shape[1]
+        xdt = _dtype_code(x.dtype)
+        if x_perm is None:
+            raise ValueError("moe_permute_noalloc: x_perm is required with x")
+        _need("moe_permute_noalloc", "x", x, (T, d), x.dtype)
+        _need("moe_permute_noalloc", "x_perm", x_perm, (T * k, d), x.dtype)
+    _dev(topk_idx, x, x_perm, counts, offsets, src_token, inv_pos)
+    _ok("moe_permute_noalloc", _lib.load().moe_permute_noalloc(
+        _p(topk_idx), T, k, e_begin, e_count, _p(x), d, xdt, _p(x_perm), _p(counts),
+        _p(offsets), _p(src_token), _p(inv_pos), _s(stream)))
     return PermuteResult(counts, offsets, src_token, inv_pos, x_perm)
 
 

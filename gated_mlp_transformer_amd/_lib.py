@@ -39,6 +39,9 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i64, _c_void_p,
                            _c_void_p, _i32, _c_void_p]),
+    "moe_permute_noalloc": (_i32, [_c_void_p, _i64, _i32, _i32, _i32, _c_void_p, _i32, _i32,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p]),
     "moe_dispatch_masked": (_i32, [_c_void_p, _i64, _i32, _i32, _i32, _i32, _c_void_p,
                                    _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "grouped_gate_up_masked": (_i32, [_c_void_p, _c_void_p, _i64, _c_void_p, _i32, _i32, _i32,

@@ -121,6 +121,30 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin, 
   return finish();
 }
 
+int moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
+                        int32_t e_count, const void* x, int32_t d, int32_t x_dtype, void* x_perm,
+                        int32_t* counts, int32_t* offsets, int32_t* src_token, int32_t* inv_pos,
+                        void* stream) {
+  // the checks of moe_permute, then the scratch size instead of a workspace
+  if (!counts || !offsets) return MF_EINVAL;
+  if (T < 0 || k < 1 || e_begin < 0 || e_count < 1) return MF_EINVAL;
+  if (T > 0 && (!topk_idx || !src_token || !inv_pos)) return MF_EINVAL;  // NULL only if empty
+  if (k > 8 || e_count > 256 || T > kI32Max / 8) return MF_EUNSUPPORTED;
+  if (mf::permute_workspace_bytes(T, e_count) > mf::kPermuteScratchBytes) return MF_EUNSUPPORTED;
+  int64_t row_bytes = 0;
+  if (x != nullptr && T > 0) {
+    if (!x_perm || d <= 0) return MF_EINVAL;
+    if (x_dtype != MF_BF16 && x_dtype != MF_F32) return MF_EINVAL;
+    row_bytes = static_cast<int64_t>(d) * (x_dtype == MF_BF16 ? 2 : 4);
+    if (row_bytes % 16 != 0 || !a16(x) || !a16(x_perm)) return MF_EUNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if (mf::permute_scratch(&ws) != 0) return MF_EHIP;
+  mf::launch_permute(topk_idx, T, k, e_begin, e_count, T > 0 ? x : nullptr, row_bytes, x_perm,
+                     counts, offsets, src_token, inv_pos, ws, S(stream));
+  return finish();
+}
+
 int moe_dispatch_masked(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
                         int32_t e_count, int32_t cap, int32_t* counts, int32_t* row_index,
                         int32_t* pos, void* workspace, size_t workspace_bytes, void* stream) {

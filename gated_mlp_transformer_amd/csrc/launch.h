@@ -18,6 +18,12 @@ void launch_route(const void* x, const void* w_r, const float* bias, int64_t T,
                   hipStream_t s);
 
 size_t permute_workspace_bytes(int64_t T, int e_count);
+// Size of the static device scratch array of the allocation-free permutation:
+// room for the count tables of ceil(T / 256) * e_count <= 65536.
+constexpr size_t kPermuteScratchBytes = 2 * 65536 * sizeof(int32_t) + 256;
+// Device address of that array on the current device (looked up once per
+// device); 0 on success, -1 if the runtime could not provide it.
+int permute_scratch(void** ptr);
 void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_count,
                     const void* x, int64_t row_bytes, void* x_perm, int32_t* counts,
                     int32_t* offsets, int32_t* src_token, int32_t* inv_pos,

@@ -18,6 +18,8 @@
 //               to e.
 //   3. gather:  x_perm[r] = x[src_token[r]], 16-byte copies (only when x is
 //               given).
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -366,6 +368,39 @@ void launch_permute(const int32_t* idx, int64_t T, int k, int e_begin, int e_cou
         static_cast<const char*>(x), T, row_bytes, src_token, offsets, e_count, max_rows,
         static_cast<char*>(x_perm));
   }
+}
+
+// ---- the allocation-free variant: a static device scratch array -----------
+//
+// For callers that cannot allocate (code under graph capture, serving loops):
+// the count tables live in a file-scope device array instead of a caller
+// workspace. Every GPU the library runs on holds its own copy of the array
+// until the process ends; its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// handed to kernels. The kernels write every count-table entry they later read
+// (nothing must start at zero), so no clearing is needed; calls that overlap
+// on one GPU share the array and race.
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+__device__ __align__(256) char scratch[kPermuteScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+int permute_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return -1;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 }  // namespace mf

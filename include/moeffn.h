@@ -167,6 +167,27 @@ int moe_permute(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * moe_permute_noalloc - moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, outputs,
+ * results and errors as moe_permute, minus workspace / workspace_bytes.
+ *
+ * Its count tables live in a static device array of the library (about
+ * 512 KiB, held on every GPU the library runs on until the process ends),
+ * whose address is looked up once per device on the first call there. It
+ * allocates nothing. Limit: ceil(T / 256) * e_count <= 65536 (for instance
+ * T <= 65536 with 256 local experts); larger calls return MF_EUNSUPPORTED
+ * with nothing enqueued. Every call on one GPU shares that GPU's array, so
+ * calls that may overlap on one GPU (different streams, different host
+ * threads) race: order them. Returns MF_EHIP if the array's address cannot be
+ * obtained.
+ */
+int moe_permute_noalloc(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e_begin,
+                        int32_t e_count, const void* x, int32_t d, int32_t x_dtype, void* x_perm,
+                        int32_t* counts, int32_t* offsets, int32_t* src_token, int32_t* inv_pos,
+                        void* stream);
+
+/*
  * moe_dispatch_masked - the masked (fixed-capacity) layout of the routing
  * slots, the decode variant of the permutation ("「赤兔」Chitu 框架深度解读（七）：MoE":
  * the decode experts run as a masked GEMM (deepgemm_masked), the decode

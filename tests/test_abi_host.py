@@ -69,6 +69,21 @@ def test_rmsnorm_validation(lib):
     assert lib.rmsnorm(P, P, P, 0, 64, 1e-5, BF16, N) == MF_OK
 
 
+def test_permute_noalloc_validation(lib):
+    # the allocation-free permutation rejects what moe_permute rejects, and calls
+    # whose count tables exceed its static array, before any launch
+    assert lib.moe_permute_noalloc(P, 4, 8, 0, 16, N, 0, BF16, N, N, P, P, P, N) == MF_EINVAL
+    assert lib.moe_permute_noalloc(P, 4, 8, 0, 16, N, 0, BF16, N, P, N, P, P, N) == MF_EINVAL
+    assert lib.moe_permute_noalloc(N, 4, 8, 0, 16, N, 0, BF16, N, P, P, P, P, N) == MF_EINVAL
+    assert lib.moe_permute_noalloc(P, 4, 9, 0, 16, N, 0, BF16, N, P, P, P, P, N) == MF_EUNSUPPORTED
+    assert lib.moe_permute_noalloc(P, 4, 8, 0, 257, N, 0, BF16, N, P, P, P, P, N) == MF_EUNSUPPORTED
+    # 257 token blocks x 256 experts > 65536 count-table entries
+    assert lib.moe_permute_noalloc(P, 65537, 8, 0, 256, N, 0, BF16, N, P, P, P, P, N) \
+        == MF_EUNSUPPORTED
+    # rows to gather with a row size that is not a multiple of 16 bytes
+    assert lib.moe_permute_noalloc(P, 4, 8, 0, 16, P, 4, BF16, P, P, P, P, P, N) == MF_EUNSUPPORTED
+
+
 def test_pack_validation(lib):
     assert lib.packed_weights_bytes(2, 40, 64, BF16) == 2 * 64 * 64 * 2   # 40 rows -> 2 blocks of 32
     assert lib.packed_weights_bytes(1, 20, 128, FP8) == 32 * 128          # 20 rows -> 2 blocks of 16
