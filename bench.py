@@ -76,14 +76,15 @@ def parse():
 def moe_work(T, d, f, E, k, S, active, ec, welt, act_fp8=False):
     """Algorithmic bytes / flops per stage of one MoE FFN step (each tensor once).
 
-    With fp8 activations the gate/up stage also quantises V (read 2d, write
-    d + d/32 bytes per token) and reads the fp8 rows, and the down stage
-    quantises the live rows of H and reads them as fp8."""
+    With fp8 activations the RMSNorm pass also writes V's fp8 codes and group
+    scales (d + d/32 bytes per token), the gate/up stage reads the fp8 rows,
+    and the down stage quantises the live rows of H and reads them as fp8."""
     sc = 0 if welt == 2 else 4 * (f // 128) * (d // 128)  # fp8 scales per matrix
     if act_fp8:
         w = moe_work(T, d, f, E, k, S, active, ec, welt)
-        w["grouped_gate_up"]["bytes"] = (active * (2 * f * d + 2 * sc) + T * d * 2 + T * d
-                                         + T * d // 32 + S * d + S * d // 32 + S * f * 2 + S * 4)
+        w["rmsnorm"]["bytes"] += T * d + T * d // 32
+        w["grouped_gate_up"]["bytes"] = (active * (2 * f * d + 2 * sc) + S * d + S * d // 32
+                                         + S * f * 2 + S * 4)
         w["grouped_down"]["bytes"] = (active * (d * f + sc) + S * f * 2 + S * f + S * f // 32
                                       + S * f + S * f // 32 + S * d * 2)
         return w

@@ -27,7 +27,8 @@ MF_F32, MF_BF16, MF_FP8_E4M3 = 0, 1, 2
 _lib.load()  # fail loudly at import if the HIP library is missing
 
 __all__ = [
-    "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "moe_route_workspace_size",
+    "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "rmsnorm_quantize_fp8",
+    "moe_route_workspace_size",
     "moe_route",
     "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc", "moe_dispatch_masked", "MaskedDispatch",
     "grouped_gate_up_masked", "grouped_down_masked", "quantize_fp8_rows", "grouped_gate_up_a8",
@@ -116,6 +117,29 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5,
     _ok("rmsnorm", _lib.load().rmsnorm(_p(x), _p(gamma), _p(out), T, d, eps,
                                        _dtype_code(x.dtype), _s(stream)))
     return out
+
+
+def rmsnorm_quantize_fp8(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5, *,
+                         out: Optional[torch.Tensor] = None, q: Optional[torch.Tensor] = None,
+                         scales: Optional[torch.Tensor] = None, stream=None):
+    """rmsnorm (bf16) plus, in the same pass, quantize_fp8_rows of its output.
+    Returns (y bf16 [T, d], q uint8 [T, d], scales f32 [T, d/128])."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("rmsnorm_quantize_fp8: x must be bf16 [T, d]")
+    T, d = x.shape
+    out = torch.empty_like(x) if out is None else out
+    q = torch.empty((T, d), dtype=torch.uint8, device=x.device) if q is None else q
+    if scales is None:
+        scales = torch.empty((T, max(d // 128, 0)), dtype=torch.float32, device=x.device)
+    n = "rmsnorm_quantize_fp8"
+    _need(n, "gamma", gamma, (d,), torch.bfloat16)
+    _need(n, "out", out, (T, d), torch.bfloat16)
+    _need(n, "q", q, (T, d), torch.uint8)
+    _need(n, "scales", scales, (T, max(d // 128, 0)), torch.float32)
+    _dev(x, gamma, out, q, scales)
+    _ok(n, _lib.load().rmsnorm_quantize_fp8(_p(x), _p(gamma), _p(out), _p(q), _p(scales), T, d,
+                                            eps, _s(stream)))
+    return out, q, scales
 
 
 class PackedWeights(NamedTuple):
@@ -615,10 +639,10 @@ class MoEFFNLayer:
 
         ``act_fp8`` (block-fp8 weights only): the expert GEMMs take fp8
         activations, as the block-fp8 prefill variant does: V is quantised per
-        token and 1x128 group before the gate/up GEMM and H before the down
-        GEMM (quantize_fp8_rows), and the GEMMs run on the fp8 MFMA
-        (grouped_gate_up_a8 / grouped_down_a8). Each quantisation is timed with
-        the GEMM it feeds.
+        token and 1x128 group in the RMSNorm pass (rmsnorm_quantize_fp8; by
+        quantize_fp8_rows when the layer has no RMSNorm) and H before the down
+        GEMM (quantize_fp8_rows, timed with the down GEMM), and the GEMMs run
+        on the fp8 MFMA (grouped_gate_up_a8 / grouped_down_a8).
 
         ``layout="masked"`` (the decode variant): moe_dispatch_masked replaces
         the permutation (fixed blocks of ``cap`` rows per local expert, default
@@ -681,7 +705,11 @@ class MoEFFNLayer:
 
         mark(0)
         v = x
-        if self.gamma is not None:
+        if self.gamma is not None and self.act_fp8 and self.layout == "contiguous":
+            # V and its per-token fp8 activations in one pass
+            v, _, _ = rmsnorm_quantize_fp8(x, self.gamma, self.eps, out=self.v, q=self.vq,
+                                           scales=self.vs, stream=s)
+        elif self.gamma is not None:
             v = rmsnorm(x, self.gamma, self.eps, out=self.v, stream=s)
         mark(1)
         moe_route(v, self.w_r, self.bias, self.k, self.idx, self.topk_w, self.route_ws, stream=s)
@@ -706,7 +734,8 @@ class MoEFFNLayer:
                     workspace=self.workspace, stream=s)
         mark(3)
         if self.act_fp8:
-            quantize_fp8_rows(v, q=self.vq, scales=self.vs, stream=s)
+            if self.gamma is None:  # no RMSNorm pass to fold the quantisation into
+                quantize_fp8_rows(v, q=self.vq, scales=self.vs, stream=s)
             grouped_gate_up_a8(self.vq, self.vs, self.offsets, self.w[0], self.w[1], self.s[0],
                                self.s[1], row_index=self.src_token, h_out=self.h, stream=s)
             mark(4)

@@ -20,6 +20,8 @@ _SIGNATURES = {
     "mf_status_string": (ctypes.c_char_p, [_i32]),
     "mf_version": (ctypes.c_char_p, []),
     "rmsnorm": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _f32, _i32, _c_void_p]),
+    "rmsnorm_quantize_fp8": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _i64, _i32, _f32, _c_void_p]),
     "packed_weights_bytes": (_size, [_i64, _i32, _i32, _i32]),
     "pack_weights": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p]),
     "moe_route_workspace_size": (_size, [_i64, _i32, _i32]),

@@ -53,6 +53,20 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d, flo
   return finish();
 }
 
+int rmsnorm_quantize_fp8(const void* x, const void* gamma, void* y, void* q, float* scales,
+                         int64_t T, int32_t d, float eps, void* stream) {
+  if (T < 0 || d <= 0 || !(eps >= 0.f) || !isfinite(eps)) return MF_EINVAL;
+  if (d % 128 != 0 || d > 8192) return MF_EUNSUPPORTED;
+  if (T == 0) return MF_OK;  // zero-size buffers may be NULL
+  if (!x || !gamma || !y || !q || !scales) return MF_EINVAL;
+  if (!a16(x) || !a16(gamma) || !a16(y) || reinterpret_cast<uintptr_t>(q) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+    return MF_EUNSUPPORTED;
+  if ((T + 3) / 4 > 0xFFFFFFFFLL) return MF_EUNSUPPORTED;
+  mf::launch_rmsnorm(x, gamma, y, T, d, eps, true, S(stream), static_cast<uint8_t*>(q), scales);
+  return finish();
+}
+
 size_t packed_weights_bytes(int64_t groups, int32_t N, int32_t K, int32_t dtype) {
   if (groups < 0 || N <= 0 || K <= 0) return 0;
   if (dtype == MF_BF16 && K % 16 == 0) return mf::packed_bytes(groups, N, K, false);

@@ -8,8 +8,11 @@
 
 namespace mf {
 
+// q / qs (bf16 only, d % 128 == 0, or both nullptr): also the per-token fp8
+// codes [T, d] and group scales [T, d/128] of the bf16 output
 void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
-                    float eps, bool bf16, hipStream_t s);
+                    float eps, bool bf16, hipStream_t s, uint8_t* q = nullptr,
+                    float* qs = nullptr);
 
 int route_splits(int64_t T, int d);
 size_t route_workspace_bytes(int64_t T, int d, int E);

@@ -6,14 +6,67 @@
 // (the next row's are loaded while the current one is reduced and written),
 // so a row is read from HBM once and written once (HBM-bound: 2 * d *
 // sizeof(T) bytes per row).
+//
+// The bf16 kernels can also emit the row's per-token fp8 activations for the
+// block-fp8 prefill variant in the same pass: the bf16 output values are cut
+// into groups of 128 channels (16 lanes' 16-byte slices of one vector index,
+// i.e. one DPP row), the group scale is s = max(amax, 1e-4) / 448 and each
+// code is the E4M3FN value nearest to y / s (ties to even), in fp32 with IEEE
+// division -- the quantiser's rule applied to the bf16 values it would read.
 #include "common.h"
 #include "launch.h"
 
 namespace mf {
 
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row_umax(uint32_t v) {
+  // lanes outside the source row receive 0, the identity of the unsigned max
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return v > o ? v : o;
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_encode2(float a, float b, float s, uint32_t old) {
+  a = fminf(fmaxf(a / s, -448.0f), 448.0f);
+  b = fminf(fmaxf(b / s, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), HI));
+}
+
+// fp8 codes of the eight bf16 values in o (this lane's slice of a 128-channel
+// group held by the lane's 16-lane DPP row) to q8 (8 bytes); the lane at the
+// start of the row writes the group scale to *scale.
+__device__ __forceinline__ void quant_group_store(const u32x4& o, int lane, uint8_t* q8,
+                                                  float* scale) {
+  float f[8];
+  unpack_bf16x8(o, f);
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  uint32_t mb = __float_as_uint(m);  // non-negative floats order as unsigned integers
+  mb = dpp_row_umax<0xB1>(mb);   // quad_perm [1,0,3,2]
+  mb = dpp_row_umax<0x4E>(mb);   // quad_perm [2,3,0,1]
+  mb = dpp_row_umax<0x141>(mb);  // row_half_mirror
+  mb = dpp_row_umax<0x140>(mb);  // row_mirror: every lane of the row has its max
+  const float sc = fmaxf(__uint_as_float(mb), 1e-4f) / 448.0f;
+  u32x2 out;
+  out[0] = fp8_encode2<false>(f[0], f[1], sc, 0u);
+  out[0] = fp8_encode2<true>(f[2], f[3], sc, out[0]);
+  out[1] = fp8_encode2<false>(f[4], f[5], sc, 0u);
+  out[1] = fp8_encode2<true>(f[6], f[7], sc, out[1]);
+  *reinterpret_cast<u32x2*>(q8) = out;
+  if ((lane & 15) == 0) *scale = sc;
+}
+
+}  // namespace
+
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __restrict__ gamma,
-                                                      T* y, int64_t rows, int d, float eps) {
+                                                      T* y, int64_t rows, int d, float eps,
+                                                      uint8_t* __restrict__ q,
+                                                      float* __restrict__ qs) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
   const int lane = threadIdx.x % kWave;
   const int nvec = d / EPV;
@@ -75,6 +128,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 #pragma unroll
           for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
           o = pack_bf16x8(res);
+          if (q != nullptr)  // whole 16-lane rows take this branch together (d % 128 == 0)
+            quant_group_store(o, lane, q + row * d + static_cast<int64_t>(vi) * 8,
+                              qs + row * (d / 128) + vi / 16);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -95,7 +151,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 // row per wave at a time, gamma re-read from cache per row.
 template <typename T, int NV>
 __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
-                                                           T* y, int64_t rows, int d, float eps) {
+                                                           T* y, int64_t rows, int d, float eps,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ qs) {
   const int lane = threadIdx.x % kWave;
   const char* gr = reinterpret_cast<const char*>(gamma) + lane * 16;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
@@ -143,6 +201,11 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
 #pragma unroll
         for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
         o = pack_bf16x8(res);
+        if (q != nullptr) {
+          const int vi = lane + i * kWave;
+          quant_group_store(o, lane, q + row * d + static_cast<int64_t>(vi) * 8,
+                            qs + row * (d / 128) + vi / 16);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -157,7 +220,7 @@ namespace {
 
 template <typename T>
 bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d, float eps,
-                 hipStream_t s) {
+                 uint8_t* q, float* qs, hipStream_t s) {
   const int per_lane = d * static_cast<int>(sizeof(T)) / (16 * kWave);  // vectors per lane
   if (d * static_cast<int>(sizeof(T)) % (16 * kWave) != 0) return false;
   int64_t blocks = (rows + 3) / 4;
@@ -167,14 +230,14 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
   auto* gp = static_cast<const T*>(gamma);
   auto* yp = static_cast<T*>(y);
   switch (per_lane) {
-    case 1: rmsnorm_full_kernel<T, 1><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
-    case 2: rmsnorm_full_kernel<T, 2><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
-    case 4: rmsnorm_full_kernel<T, 4><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
-    case 8: rmsnorm_full_kernel<T, 8><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
-    case 16: rmsnorm_full_kernel<T, 16><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps); return true;
+    case 1: rmsnorm_full_kernel<T, 1><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 2: rmsnorm_full_kernel<T, 2><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 4: rmsnorm_full_kernel<T, 4><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 8: rmsnorm_full_kernel<T, 8><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 16: rmsnorm_full_kernel<T, 16><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
     case 32:  // f32 rows of 8192
       if constexpr (sizeof(T) == 4) {
-        rmsnorm_full_kernel<T, 32><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps);
+        rmsnorm_full_kernel<T, 32><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs);
         return true;
       }
       return false;
@@ -185,9 +248,9 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
 }  // namespace
 
 void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
-                    float eps, bool bf16, hipStream_t s) {
-  if (bf16 ? launch_full<bf16_t>(x, gamma, y, T, d, eps, s)
-           : launch_full<float>(x, gamma, y, T, d, eps, s))
+                    float eps, bool bf16, hipStream_t s, uint8_t* q, float* qs) {
+  if (bf16 ? launch_full<bf16_t>(x, gamma, y, T, d, eps, q, qs, s)
+           : launch_full<float>(x, gamma, y, T, d, eps, nullptr, nullptr, s))
     return;
   // about two rows per wave: enough waves to fill the chip, each with a row in flight
   int64_t blocks = (T + 7) / 8;
@@ -200,15 +263,18 @@ void launch_rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int d,
     auto* xp = static_cast<const bf16_t*>(x);
     auto* gp = static_cast<const bf16_t*>(gamma);
     auto* yp = static_cast<bf16_t*>(y);
-    if (small) rmsnorm_kernel<bf16_t, 8><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
-    else rmsnorm_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
+    if (small) rmsnorm_kernel<bf16_t, 8><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps, q, qs);
+    else rmsnorm_kernel<bf16_t, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps, q, qs);
   } else {
     auto* xp = static_cast<const float*>(x);
     auto* gp = static_cast<const float*>(gamma);
     auto* yp = static_cast<float*>(y);
-    if (small) rmsnorm_kernel<float, 8><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
-    else if (d * 4 <= 16 * 16 * kWave) rmsnorm_kernel<float, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
-    else rmsnorm_kernel<float, 32><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps);
+    if (small)
+      rmsnorm_kernel<float, 8><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps, nullptr, nullptr);
+    else if (d * 4 <= 16 * 16 * kWave)
+      rmsnorm_kernel<float, 16><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps, nullptr, nullptr);
+    else
+      rmsnorm_kernel<float, 32><<<grid, 256, 0, s>>>(xp, gp, yp, T, d, eps, nullptr, nullptr);
   }
 }
 

@@ -2,28 +2,42 @@
 //   z = x W_r^T, s = sigmoid(z), I = Top8(s + b), w_i = s_i / sum_{j in I} s_j.
 //
 // Two kernels:
-//  1. logits: z = x W_r^T on the bf16 MFMA GEMM core (128-token tiles against
-//     all E <= 256 router rows, fp32 accumulation). The d-long contraction is
-//     split into `splits` equal ranges so that about 256 workgroups run even
-//     for a few thousand tokens; split y writes its fp32 partial logits to
-//     workspace[y][T][E]. Splitting K instead of E keeps every workgroup's
-//     W_r traffic at 1/splits of the router weight.
+//  1. logits: z = x W_r^T with fp32 accumulation, the d-long contraction split
+//     into `splits` equal ranges so that about 256 workgroups run; split y
+//     writes its fp32 partial logits to workspace[y][T][E].
+//     - Many tokens: the bf16 MFMA GEMM core (128-token tiles against all
+//       E <= 256 router rows). Splitting K instead of E keeps every
+//       workgroup's W_r traffic at 1/splits of the router weight.
+//     - Few tokens (decode): one wavefront per 32 tokens x 32 experts x one
+//       K range, one 32x32x16 MFMA tile, so that the 2 MB router weight is
+//       spread over ~256 workgroups (E/32 expert blocks x K ranges) instead
+//       of a handful of 128-token tiles. Each lane loads its token row's
+//       64-byte runs (four 16-byte loads per 64-deep step) and, for the same
+//       permuted contraction order, the matching 16-byte slots of the packed
+//       weight fragments; every load of the K range is in flight before the
+//       first MFMA.
 //  2. select: one wavefront per token sums the partials in split order (fixed
 //     order: deterministic), applies the sigmoid and the bias, and picks the
 //     top 8 by eight rounds of a wave-wide arg-max on (key descending, id
 //     ascending); the ids are emitted ascending with w = s / sum(s).
+//     Lane l holds experts 4l .. 4l+3, so each split's partials of a token
+//     arrive with one 16-byte load per lane (1 KB per wave instruction).
 //     A round takes the wave-wide maximum of the keys (mapped to
 //     order-preserving unsigned integers) with DPP max steps at register
 //     speed, then the lowest expert id that holds it as a second DPP
 //     maximum (of 256 - id over the lanes' candidates equal to the key
-//     maximum; a lane holds experts lane + 64c). Only that candidate is
-//     retired, so equal keys are taken in ascending id order over the rounds.
+//     maximum). Only that candidate is retired, so equal keys are taken in
+//     ascending id order over the rounds. A winner's output slot is its rank
+//     among the winners by id (popcounts of per-slot ballots), and the eight
+//     scores are summed in that order.
 #include "common.h"
 #include "launch.h"
 
 namespace mf {
 
 namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kTargetWGs = 256;   // one workgroup per CU of an MI355X
 constexpr int kTokTile = 128;     // token rows per logits tile
@@ -60,9 +74,21 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 
 }  // namespace
 
+// Token counts up to this take the few-token logits kernel.
+constexpr int64_t kSmallT = 256;
+
 int route_splits(int64_t T, int d) {
+  int ks = 1;
+  if (T <= kSmallT) {
+    // (T/32) x (E/32) x splits workgroups with E up to 256; each split's K
+    // range a multiple of 64
+    const int64_t tiles = ((T + 31) / 32) * 8;
+    while ((d / 64) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs && ks * 2 <= kMaxSplits)
+      ks *= 2;
+    return ks;
+  }
   const int64_t tiles = (T + kTokTile - 1) / kTokTile;
-  int ks = 1;  // each split's K range must stay a multiple of 256
+  // each split's K range must stay a multiple of 256
   while ((d / 256) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs && ks * 2 <= kMaxSplits) ks *= 2;
   return ks;
 }
@@ -71,95 +97,188 @@ size_t route_workspace_bytes(int64_t T, int d, int E) {
   return static_cast<size_t>(route_splits(T, d)) * static_cast<size_t>(T) * E * sizeof(float);
 }
 
-template <int SPLITS>
-__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ zp,
-                                                           const float* __restrict__ bias,
-                                                           int64_t T, int E,
-                                                           int32_t* __restrict__ idx_out,
-                                                           float* __restrict__ w_out) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (t >= T) return;
-  const int64_t split_stride = T * E;
-  // All partial logits are loaded before any is added (independent loads in
-  // flight together), then summed in split order. The loads are
-  // unconditional (experts past E re-read expert E-1 and are masked below):
-  // a load under a per-lane condition would become a branch with its own wait.
-  float part[SPLITS][4];
+// Few-token logits: one wavefront per (32 tokens, 32 experts, K range z).
+// Lane l owns token row t0 + l%32 and lane group g = l/32. For 64-deep step m
+// it loads the 64 bytes k0 + 64m + 32g .. +32 of its row; MFMA c of the step
+// then takes elements 8c .. 8c+7 of them, i.e. lane group g, element v of
+// MFMA c stands for k = k0 + 64m + 32g + 8c + v. The weight operand uses the
+// same order: that k lives in packed fragment kb = k / 16 at slot
+// (l%32) + 32 ((k / 8) % 2) = (l%32) + 32 (c % 2). The dot products are
+// unchanged by the common permutation.
+__global__ __launch_bounds__(64) void route_logits_small_kernel(
+    const bf16_t* __restrict__ x, const char* __restrict__ w_r, int T, int d, int E, int kc,
+    float* __restrict__ zp) {
+  constexpr int FRAG = 1024;
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32, z = blockIdx.z;
+  const int lr = lane & 31, g = lane >> 5;
+  const int t = min(t0 + lr, T - 1);  // rows past T re-read row T-1 and are not stored
+  const int k0 = z * kc;
+  const char* xa = reinterpret_cast<const char*>(x) + (static_cast<int64_t>(t) * d + k0 + 32 * g) * 2;
+  // packed weights: fragment (nb, kb) at (nb * d/16 + kb) * 1 KB; slot l' at l' * 16 B
+  const int nb = blockIdx.y;
+  const char* wb = w_r + (static_cast<int64_t>(nb) * (d / 16) + k0 / 16 + 2 * g) * FRAG + lr * 16;
+  f32x16 acc = f32x16{};
+  for (int m0 = 0; m0 < kc; m0 += 256) {  // four 64-deep steps in flight at a time
+    const int nm = min(4, (kc - m0) / 64);
+    u32x4 a[4][4], b[4][4];
 #pragma unroll
-  for (int y = 0; y < SPLITS; ++y)
+    for (int m = 0; m < 4; ++m) {
+      if (m < nm) {
+        const int mm = m0 / 64 + m;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = min(lane + 64 * c, E - 1);
-      part[y][c] = zp[y * split_stride + t * E + e];
+        for (int c = 0; c < 4; ++c) {
+          a[m][c] = ld16(xa + (64 * mm + 8 * c) * 2);
+          b[m][c] = ld16(wb + (4 * mm + c / 2) * static_cast<int64_t>(FRAG) + (c % 2) * 512);
+        }
+      }
     }
-  // candidates of this lane: experts lane + 64c, the key s + b mapped to an
-  // order-preserving unsigned integer; experts past E and retired winners
-  // hold 0, below every valid key
-  float sc[4];
-  uint32_t key[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    float z = 0.f;
+    for (int m = 0; m < 4; ++m)
+      if (m < nm)
 #pragma unroll
-    for (int y = 0; y < SPLITS; ++y) z += part[y][c];
-    sc[c] = sigmoidf_(z);
-    key[c] = e < E ? order_key(sc[c] + bias[min(e, E - 1)]) : 0u;
+        for (int c = 0; c < 4; ++c)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[m][c]),
+                                                        __builtin_bit_cast(bf16x8, a[m][c]), acc,
+                                                        0, 0, 0);
   }
+  // lane holds token t0 + lr and experts e0 + 8q + 4g + r (q, r = 0..3)
+  if (t0 + lr >= T) return;
+  float* zr = zp + (static_cast<int64_t>(z) * T + t0 + lr) * E;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = e0 + 8 * q + 4 * g;
+    if ((E & 3) == 0 && e + 3 < E) {
+      st16(zr + e, u32x4{__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
+                         __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3])});
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (e + r < E) zr[e + r] = acc[4 * q + r];
+    }
+  }
+}
+
+// Top-8 of one token held by one wavefront: lane l holds experts 4l + c
+// (c = 0..3) as order-preserving keys of s + b (0 for experts past E) and
+// their scores s. Writes the ids ascending to idx[0..7] and w = s / sum(s) to
+// w[0..7]; sc8 is this wave's 8-float LDS staging.
+__device__ __forceinline__ void select_top8(uint32_t (&key)[4], const float (&sc)[4], int lane,
+                                            int32_t* __restrict__ idx, float* __restrict__ w,
+                                            float* sc8) {
+  const int eb = 4 * lane;
   // Eight rounds; a round takes the wave-wide maximum key m, then the lowest
   // expert id holding it as a second wave-wide maximum, of 256 - e over each
   // lane's candidates equal to m (all in VALU/DPP: no ballot chains on the
-  // CU's one scalar unit, which all the resident token waves share). The
-  // owner lane retires the winner and flags it.
-  uint32_t won = 0;  // bit c: expert lane + 64c was selected
+  // CU's one scalar unit, which all the resident waves share). The owner
+  // lane retires the winner and flags it.
+  uint32_t won = 0;  // bit c: expert 4 lane + c was selected
 #pragma unroll
   for (int round = 0; round < 8; ++round) {
     const uint32_t m = wave_umax(max(max(key[0], key[1]), max(key[2], key[3])));
     uint32_t cand = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      cand = max(cand, key[c] == m ? 256u - static_cast<uint32_t>(lane + 64 * c) : 0u);
+      cand = max(cand, key[c] == m ? 256u - static_cast<uint32_t>(eb + c) : 0u);
     const int e = 256 - static_cast<int>(wave_umax(cand));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bool hit = lane + 64 * c == e;  // only the owner lane's slot matches
+      const bool hit = eb + c == e;  // only the owner lane's slot matches
       key[c] = hit ? 0u : key[c];
       won |= hit ? 1u << c : 0u;
     }
   }
-  // The winners in ascending id order (slot c, then lane): rank r goes to
-  // lane r of the outputs, and the scores are summed in that order.
-  int out_e = 0;
-  float out_s = 0.f, sum = 0.f;
+  // Rank of a winner among the winners by id: the winners of the lanes below
+  // plus this lane's winners at lower slots.
+  const uint64_t below = (1ull << lane) - 1ull;
   int r = 0;
 #pragma unroll
+  for (int c = 0; c < 4; ++c)
+    r += __popcll(__builtin_amdgcn_ballot_w64((won >> c) & 1u) & below);
+#pragma unroll
   for (int c = 0; c < 4; ++c) {
-    uint64_t mk = __builtin_amdgcn_ballot_w64((won >> c) & 1u);
-    while (mk) {
-      const int l = __builtin_ctzll(mk);
-      mk &= mk - 1;
-      const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc[c]), l));
-      if (lane == r) {
-        out_e = l + 64 * c;
-        out_s = sv;
-      }
-      sum += sv;
+    if ((won >> c) & 1u) {
+      idx[r] = eb + c;
+      sc8[r] = sc[c];
       ++r;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < 8) {
-    idx_out[t * 8 + lane] = out_e;
-    w_out[t * 8 + lane] = out_s / sum;
+    float sum = 0.f;  // in ascending id order
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += sc8[i];
+    w[lane] = sc8[lane] / sum;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int SPLITS>
+__global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ zp,
+                                                           const float* __restrict__ bias,
+                                                           int64_t T, int E,
+                                                           int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out) {
+  __shared__ float s_sc[4][8];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (t >= T) return;
+  const int64_t split_stride = T * E;
+  // candidates of this lane: experts 4 lane + c
+  const int eb = 4 * lane;
+  // All partial logits are loaded before any is added (independent loads in
+  // flight together), then summed in split order. With E a multiple of 4 each
+  // split is one 16-byte load per lane (lanes past E re-read the last four
+  // experts and are masked below); otherwise four element loads, clamped the
+  // same way. The loads are unconditional: a load under a per-lane condition
+  // would become a branch with its own wait.
+  float part[SPLITS][4];
+  if ((E & 3) == 0) {
+    const int ev = min(eb, E - 4);
+#pragma unroll
+    for (int y = 0; y < SPLITS; ++y) {
+      const u32x4 v = ld16(zp + y * split_stride + t * E + ev);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) part[y][c] = __uint_as_float(v[c]);
+    }
+  } else {
+#pragma unroll
+    for (int y = 0; y < SPLITS; ++y)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) part[y][c] = zp[y * split_stride + t * E + min(eb + c, E - 1)];
+  }
+  float sc[4];
+  uint32_t key[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = eb + c;
+    float z = 0.f;
+#pragma unroll
+    for (int y = 0; y < SPLITS; ++y) z += part[y][c];
+    sc[c] = sigmoidf_(z);
+    key[c] = e < E ? order_key(sc[c] + bias[min(e, E - 1)]) : 0u;
+  }
+  select_top8(key, sc, lane, idx_out + t * 8, w_out + t * 8, s_sc[wave]);
 }
 
 void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, int d, int E,
                   int32_t* idx, float* w, void* workspace, int num_cus, hipStream_t s) {
   const int splits = route_splits(T, d);
   float* zp = static_cast<float*>(workspace);
-  launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
+  if (T <= kSmallT) {
+    const dim3 lg(static_cast<unsigned>((T + 31) / 32), static_cast<unsigned>((E + 31) / 32),
+                  static_cast<unsigned>(splits));
+    route_logits_small_kernel<<<lg, 64, 0, s>>>(static_cast<const bf16_t*>(x),
+                                                static_cast<const char*>(w_r), static_cast<int>(T),
+                                                d, E, d / splits, zp);
+  } else {
+    launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
+  }
   const dim3 grid(static_cast<unsigned>((T + 3) / 4));
   switch (splits) {  // route_splits returns a power of two <= kMaxSplits
     case 1: route_select_kernel<1><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;

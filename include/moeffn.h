@@ -73,6 +73,24 @@ int rmsnorm(const void* x, const void* gamma, void* y, int64_t T, int32_t d,
             float eps, int32_t dtype, void* stream);
 
 /*
+ * rmsnorm_quantize_fp8 - rmsnorm (bf16) and, in the same pass, the per-token
+ * fp8 activations of its output for the block-fp8 prefill variant: y as
+ * rmsnorm writes it, and q / scales exactly as quantize_fp8_rows(y) would
+ * write them (each row of y cut into groups of 128 channels, group scale
+ * s = max(amax, 1e-4) / 448, code = the E4M3FN value nearest to y / s, ties
+ * to even, fp32 with IEEE division).
+ *
+ * "推理计算流梳理", Norm&Residual (V = RMSNorm_ffn(R)); "「赤兔」Chitu 框架深度解读
+ * （七）：MoE", 专家计算实现 / 量化支持 (FP8 GEMMs for prefill, block fp8).
+ *
+ * x, y [T, d] bf16 (y may alias x); gamma [d] bf16; q [T, d] E4M3FN codes
+ * (8-byte aligned); scales [T, d/128] f32. Requires d % 128 == 0, d <= 8192
+ * (MF_EUNSUPPORTED otherwise); eps >= 0.
+ */
+int rmsnorm_quantize_fp8(const void* x, const void* gamma, void* y, void* q, float* scales,
+                         int64_t T, int32_t d, float eps, void* stream);
+
+/*
  * packed_weights_bytes - bytes of pack_weights' output for `groups` weight
  * matrices of N rows and K columns (dtype MF_BF16 or MF_FP8_E4M3). Returns 0
  * for arguments pack_weights would reject.
@@ -121,7 +139,8 @@ size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E);
  *                           content on entry does not matter
  * Logits are bf16 x bf16 products accumulated in fp32 on MFMA (the d-long
  * contraction may be split into ranges whose fp32 partial sums are added in a
- * fixed order); s, s + b and w are fp32. Ties in s + b go to the lower id.
+ * fixed order); s, s + b and w are fp32. The result is the same run to run.
+ * Ties in s + b go to the lower id.
  * Requires k == 8, 8 <= E <= 256, d % 256 == 0.
  */
 int moe_route(const void* x, const void* w_r, const float* bias, int64_t T,

@@ -109,6 +109,11 @@ def test_route_validation(lib):
     assert call(E=257) == MF_EUNSUPPORTED
     assert call(d=64) == MF_EUNSUPPORTED          # d % 256
     assert call(T=0, x=N, wsp=N, wsb=0) == MF_OK
+    # few tokens: (T/32) x 8 x splits workgroups, K ranges multiples of 64
+    assert lib.moe_route_workspace_size(256, 4096, 256) == 4 * 256 * 256 * 4
+    assert lib.moe_route_workspace_size(64, 4096, 256) == 16 * 64 * 256 * 4
+    # many tokens: 128-token tiles x splits <= 256 workgroups
+    assert lib.moe_route_workspace_size(4096, 4096, 256) == 8 * 4096 * 256 * 4
 
 
 def test_permute_validation(lib):

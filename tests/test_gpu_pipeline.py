@@ -108,6 +108,10 @@ def check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype, *, masked=None):
     # and the GPU's H for the down GEMM
     if a8:
         vq = layer.vq.cpu().numpy().astype(np.uint8)
+        # V's fp8 codes and scales are the quantiser's on the GPU's bf16 V
+        vq_ref, vs_ref = oracle.quantize_rows(v_gpu)
+        assert np.array_equal(vq, vq_ref)
+        assert np.array_equal(layer.vs.double().cpu().numpy(), vs_ref)
         xp = oracle.dequant_rows(vq[src], layer.vs.double().cpu().numpy()[src])
         hq_ref, hs_ref = oracle.quantize_rows(to_f64(layer.h[:S]))
         assert np.array_equal(layer.hq[:S].cpu().numpy().astype(np.uint8), hq_ref)

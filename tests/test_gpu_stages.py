@@ -50,6 +50,26 @@ def test_rmsnorm(g, dtype, T, d):
     assert_fp("rmsnorm", to_f64(y), ref, **tol)
 
 
+@pytest.mark.parametrize("T,d", [(1, 128), (37, 384), (300, 4096), (5, 8192), (64, 1152)])
+def test_rmsnorm_quantize_fp8(g, T, d):
+    """The fused pass writes rmsnorm's output bit for bit and, from it, the
+    codes and scales of quantize_fp8_rows and of the oracle's quantiser."""
+    x = synth.normal((T, d), name="t.rmsq.x", sub=d, device=DEV)
+    if T > 2:
+        x[0] = 0
+        x[1, :128] = 0
+    gamma = synth.normal((d,), name="t.rmsq.g", std=0.1, mean=1.0, device=DEV)
+    y, q, sc = g.rmsnorm_quantize_fp8(x, gamma, 1e-5)
+    y_ref = g.rmsnorm(x, gamma, 1e-5)
+    q_ref, sc_ref = g.quantize_fp8_rows(y_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(q, q_ref) and torch.equal(sc, sc_ref)
+    oq, osc = oracle.quantize_rows(to_f64(y))
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(sc.double().cpu().numpy(), osc)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_rmsnorm_rows_beyond_8192_are_unsupported(g, dtype):
     x = torch.zeros((2, 8256), dtype=dtype, device=DEV)
@@ -73,7 +93,8 @@ def test_rmsnorm_in_place(g):
 @pytest.mark.parametrize("T,d,E", [(1, 256, 8), (37, 256, 12), (300, 256, 64), (257, 512, 256),
                                    (64, 4096, 256), (1000, 1024, 200), (4096, 768, 9),
                                    (129, 2048, 100), (5000, 1024, 256), (2000, 2048, 160),
-                                   (600, 768, 256)])
+                                   (600, 768, 256), (256, 4096, 256), (200, 768, 9),
+                                   (33, 1024, 162), (96, 8192, 31)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
     idx, w = g.moe_route(r["x"], g.pack_weights(r["w_r"]), r["bias"])
