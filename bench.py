@@ -41,6 +41,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PREFILL = "moe_prefill_8192tok_32exp_bf16"
 DECODE = "moe_decode_64tok_256exp_fp8"
 PREFILL_FP8 = "moe_prefill_8192tok_32exp_fp8act"
+PREFILL_FP8W = "moe_prefill_8192tok_32exp_fp8w"
 DECODE_MASKED = "moe_decode_64tok_256exp_fp8_masked"
 DENSE = "norm_tp_shard_bf16_4096"
 ROUTER = "router_4096tok_E256"
@@ -61,7 +62,7 @@ def parse():
                          "dense-shard / router-only "
                          "measurements")
     ap.add_argument("--only", choices=["prefill", "decode", "dense", "router", "prefill_fp8",
-                                       "decode_masked"],
+                                       "decode_masked", "prefill_fp8w"],
                     default=None,
                     help="run one workload only (for profiling); prints its stage times")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -635,9 +636,9 @@ def main():
             torch.cuda.synchronize()
             del src, dst
             log("[bench] copy calibration: 3 x 1 GiB device-to-device copies done")
-        if args.only in ("prefill", "decode", "prefill_fp8", "decode_masked"):
+        if args.only in ("prefill", "decode", "prefill_fp8", "decode_masked", "prefill_fp8w"):
             name = {"prefill": PREFILL, "decode": DECODE, "prefill_fp8": PREFILL_FP8,
-                    "decode_masked": DECODE_MASKED}[args.only]
+                    "decode_masked": DECODE_MASKED, "prefill_fp8w": PREFILL_FP8W}[args.only]
             res = run_moe(name, args.steps, args.warmup)
             peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
@@ -762,6 +763,14 @@ def main():
             "stages": full_report(p8["work"], p8["us"], p8["flushed"], PEAK_FP8_TFLOPS,
                                   attain=attain)}
         del p8
+        torch.cuda.empty_cache()
+        pw = run_moe(PREFILL_FP8W, ksub, args.warmup, scratch)
+        line["prefill_fp8_weights"] = {
+            "workload": PREFILL_FP8W + " (block-fp8 weights, bf16 activations)",
+            "tokens_per_s": round(T / (pw["ms"] * 1e-3), 1), "ms_per_step": round(pw["ms"], 4),
+            "graph_ms_per_step": round(pw["ms_graph"], 4), **pw["info"],
+            "stages": full_report(pw["work"], pw["us"], pw["flushed"], attain=attain)}
+        del pw
         torch.cuda.empty_cache()
         dn = run_dense(ksub, args.warmup, scratch)
         line["dense_shard"] = {

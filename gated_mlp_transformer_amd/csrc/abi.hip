@@ -209,6 +209,9 @@ void enqueue_gate_up(const void* x, const int32_t* row_index, int64_t src_rows,
   if (w_dtype == MF_BF16)
     mf::launch_gemm_gateup_bf16(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
                                 w_up, h, num_cus(), s, counts, cap);
+  else if (counts == nullptr && mf::w8_prefers_tiles(max_rows, e_count, d))
+    mf::launch_gemm_gateup_w8(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
+                              w_up, s_gate, s_up, h, num_cus(), s);
   else
     mf::launch_gemm_gateup_fp8(x, row_index, src_rows, offsets, e_count, max_rows, d, f, w_gate,
                                w_up, s_gate, s_up, h, num_cus(), s, counts, cap);
@@ -220,6 +223,8 @@ void enqueue_down(const void* h, const int32_t* offsets, int32_t e_count, int64_
   if (w_dtype == MF_BF16)
     mf::launch_gemm_down_bf16(h, offsets, e_count, max_rows, f, d, w_down, y, false, num_cus(),
                               s, counts, cap);
+  else if (counts == nullptr && mf::w8_prefers_tiles(max_rows, e_count, f))
+    mf::launch_gemm_down_w8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, num_cus(), s);
   else
     mf::launch_gemm_down_fp8(h, offsets, e_count, max_rows, f, d, w_down, s_down, y, num_cus(),
                              s, counts, cap);

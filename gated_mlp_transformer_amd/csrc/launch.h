@@ -71,6 +71,18 @@ void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count,
                           const float* s_down, void* y, int num_cus, hipStream_t s,
                           const int32_t* counts = nullptr, int cap = 0);
 
+// fp8-weight grouped GEMMs tiled for many rows per expert (gemm_w8.hip);
+// w8_prefers_tiles: whether max_rows over e_count experts and contraction K
+// take them instead of the decode kernels above.
+bool w8_prefers_tiles(int64_t max_rows, int e_count, int K);
+void launch_gemm_gateup_w8(const void* a, const int32_t* a_rows, int64_t a_src_rows,
+                           const int32_t* offsets, int e_count, int64_t max_rows, int K, int N,
+                           const void* w_gate, const void* w_up, const float* s_gate,
+                           const float* s_up, void* h, int num_cus, hipStream_t s);
+void launch_gemm_down_w8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
+                         int K, int N, const void* w_down, const float* s_down, void* y,
+                         int num_cus, hipStream_t s);
+
 // fp8 activations ([rows, K] codes + [rows, K/128] f32 group scales) against
 // block-fp8 weights on the fp8 MFMA; bf16 out (gate/up: SiLU(g) * u).
 void launch_gemm_gateup_a8(const void* a, const float* a_scale, const int32_t* a_rows,

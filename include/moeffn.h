@@ -260,7 +260,10 @@ int moe_dispatch_masked(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e
  * max_rows bounds the rows (T*k after moe_permute), so no host sync is needed.
  * GEMMs run on MFMA with bf16 operands and fp32 accumulation; SiLU(g)*u is
  * fused into the gate/up epilogue in fp32. fp8 codes are converted to bf16
- * exactly and each 128-deep partial sum is scaled in fp32.
+ * exactly and each 128-deep partial sum is scaled in fp32; with fp8 weights
+ * the work is tiled 128 rows at a time when max_rows >= 32 * e_count (and
+ * d, f <= 16384), else 16 rows per pass over each expert's weights (decode
+ * shapes, where an expert holds a few rows).
  * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 256 == 0;
  * fp8: d % 256 == 0 and f % 256 == 0.
  */

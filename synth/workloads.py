@@ -44,6 +44,9 @@ WORKLOADS = {
     "moe_prefill_8192tok_32exp_fp8act": dict(kind="moe", T=8192, d=4096, f=2048,
                                              E=256, e_begin=0, e_count=32, wdtype="fp8",
                                              act_fp8=True, zipf=ZIPF_AMPLITUDE),
+    "moe_prefill_8192tok_32exp_fp8w": dict(kind="moe", T=8192, d=4096, f=2048,
+                                           E=256, e_begin=0, e_count=32, wdtype="fp8",
+                                           zipf=ZIPF_AMPLITUDE),
     "moe_decode_64tok_256exp_fp8": dict(kind="moe", T=64, d=4096, f=2048, E=256,
                                         e_begin=0, e_count=256, wdtype="fp8",
                                         zipf=0.0),

@@ -315,6 +315,19 @@ def test_workload_prefill_8192tok_fp8_activations(g):
     assert res["S"] == to_i64(layer.counts).sum()
 
 
+def test_workload_prefill_8192tok_fp8_weights(g):
+    """The prefill workload with block-fp8 weights and bf16 activations (190
+    to 956 rows per expert: the tiled fp8-weight GEMMs), in full."""
+    spec = WORKLOADS["moe_prefill_8192tok_32exp_fp8w"]
+    inp = make_moe(spec["T"], spec["d"], spec["f"], spec["E"], spec["e_begin"], spec["e_count"],
+                   wdtype="fp8", zipf=spec["zipf"], device=DEV)
+    layer = build_layer(g, inp, spec["T"], spec["d"], spec["f"], spec["e_begin"])
+    res = check_layer(g, layer, inp, spec["T"], spec["d"], spec["f"], spec["E"],
+                      spec["e_begin"], spec["e_count"], "fp8")
+    counts = to_i64(layer.counts)
+    assert counts.min() >= 128 and res["S"] == counts.sum()
+
+
 @pytest.mark.parametrize("wdtype,T,eb,ec", [("bf16", 200, 16, 16), ("fp8", 64, 0, 64)])
 def test_masked_layout_equals_contiguous(g, wdtype, T, eb, ec):
     """The masked (fixed-capacity) layout changes where rows live, not their

@@ -213,11 +213,14 @@ def test_dispatch_masked(g, T, E, k, eb, ec, cap):
     ("bf16", [0, 1, 130, 257, 3], 300, 256, 768),
     ("bf16", [1, 33, 65, 97], 128, 256, 256),
     ("fp8", [1, 3, 0, 17, 2, 16], 20, 256, 512),
-    ("fp8", [64] * 4, 64, 512, 256),
+    ("fp8", [16] * 6, 16, 512, 256),
 ])
 def test_grouped_masked_matches_contiguous(g, wdtype, counts, cap, d, f):
     """The masked GEMMs over blocks of cap rows give, row for row, the
-    contiguous GEMMs' results (same per-row arithmetic) and match the oracle."""
+    contiguous GEMMs' results (same per-row arithmetic) and match the oracle.
+    (fp8 weights: both layouts at decode-like row counts, where the contiguous
+    call also takes the decode kernels; with more rows per expert it takes
+    the tiled kernels, whose block sums are ordered differently.)"""
     ec = len(counts)
     S = int(sum(counts))
     W = _expert_weights(ec, d, f, wdtype, seed=S + cap)
@@ -333,6 +336,11 @@ def _oracle_weights(W, e, wdtype):
     ("bf16", [3, 40], 8192, 256),     # the longest contraction: 256 K stages
     ("fp8", [3, 17, 2], 256, 8448),   # down contraction of 66 slabs: two scale chunks
     ("fp8", [9, 0, 4], 8448, 256),    # gate/up contraction of 66 slabs
+    # many rows per expert: the tiled fp8-weight kernels (128-row tiles)
+    ("fp8", [300, 0, 513, 1, 77, 256, 129], 512, 768),
+    ("fp8", [330] * 4, 1024, 512),
+    ("fp8", [200, 45], 8448, 256),    # gate/up contraction of 66 slabs, tiled
+    ("fp8", [150], 256, 8448),        # down contraction of 66 slabs, tiled
 ])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_swiglu(g, wdtype, counts, d, f, gather):
