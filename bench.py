@@ -445,20 +445,35 @@ def measure_attainable(reps=10):
         return lambda: lib.mf_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), buf.numel(), wgs,
                                              ctypes.c_void_p(out.data_ptr()), s)
 
-    hbm = max(best(read(cus * m), buf.numel()) for m in (2, 4, 8)) / 1e9
+    hbm = max(best(read(cus * m), buf.numel()) for m in (1, 2, 4)) / 1e9
+    half = buf.numel() // 2
+
+    def copy(wgs):
+        return lambda: lib.mf_probe_hbm_copy(ctypes.c_void_p(buf.data_ptr()),
+                                             ctypes.c_void_p(buf.data_ptr() + half), half, wgs, s)
+
+    hbm_rw = max(best(copy(cus * m), 2 * half) for m in (2, 4, 8)) / 1e9
     del buf
     torch.cuda.empty_cache()
-    return dict(mfma_bf16_tflop_s=round(mfma_tf, 1), hbm_gb_s=round(hbm, 1), cus=cus,
-                source="mf_probe_mfma_bf16 (back-to-back 32x32x16 bf16 MFMA, 4 waves per CU) "
-                       "and mf_probe_hbm_read (16-byte loads over 4 GiB, 2/4/8 workgroups per "
-                       f"CU), best of {reps} launches each")
+    return dict(mfma_bf16_tflop_s=round(mfma_tf, 1), hbm_gb_s=round(hbm, 1),
+                hbm_rw_gb_s=round(hbm_rw, 1), cus=cus,
+                source="mf_probe_mfma_bf16 (back-to-back 32x32x16 bf16 MFMA, 4 waves per CU), "
+                       "mf_probe_hbm_read (16-byte loads over 4 GiB, 1/2/4 workgroups per CU) "
+                       "and mf_probe_hbm_copy (2 GiB read + 2 GiB written, 2/4/8 workgroups "
+                       f"per CU), best of {reps} launches each")
+
+
+# stages whose traffic is about as much written as read: their attainable
+# bandwidth is the copy probe's, not the read probe's
+RW_STAGES = ("rmsnorm", "moe_combine")
 
 
 def full_report(work, us, flushed=None, mfma_peak=PEAK_BF16_TFLOPS, attain=None,
                 mfma_attain_key="mfma_bf16_tflop_s"):
     """Per stage: mean / median / min µs of the back-to-back steps (the mean is
     what `us` of stage_report states), the median and min of the flushed reps,
-    and the spec-peak and attainable-peak fractions of the median."""
+    and the spec-peak and attainable-peak fractions of the median (against the
+    copy probe for the read + write stages, the read probe otherwise)."""
     out = {}
     for name, w in work.items():
         if name not in us:
@@ -471,7 +486,8 @@ def full_report(work, us, flushed=None, mfma_peak=PEAK_BF16_TFLOPS, attain=None,
             gbs = w["bytes"] / t / 1e9
             r.update(gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
             if attain:
-                r["hbm_frac_attainable"] = round(gbs / attain["hbm_gb_s"], 4)
+                key = "hbm_rw_gb_s" if name in RW_STAGES and "hbm_rw_gb_s" in attain else "hbm_gb_s"
+                r["hbm_frac_attainable"] = round(gbs / attain[key], 4)
         if w.get("flops"):
             tf = w["flops"] / t / 1e12
             r.update(tflop_s=round(tf, 1), mfma_frac=round(tf / mfma_peak, 4))
@@ -659,7 +675,7 @@ def main():
     # from idle before the timed steps).
     attain = measure_attainable()
     log(f"[bench] attainable: {attain['mfma_bf16_tflop_s']} TFLOP/s bf16 MFMA, "
-        f"{attain['hbm_gb_s']} GB/s HBM read")
+        f"{attain['hbm_gb_s']} GB/s HBM read, {attain['hbm_rw_gb_s']} GB/s read + write")
     # written before every flushed rep: larger than the 256 MB last-level cache
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 

@@ -60,6 +60,7 @@ _SIGNATURES = {
                                _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "mf_probe_mfma_bf16": (_i32, [_i32, _i32, _c_void_p, _c_void_p]),
     "mf_probe_hbm_read": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p]),
+    "mf_probe_hbm_copy": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p]),
     "tp_shard_mlp": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
                             _c_void_p, _c_void_p, _c_void_p]),
 }

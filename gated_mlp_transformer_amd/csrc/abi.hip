@@ -429,4 +429,12 @@ int mf_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups, uint32
   return finish();
 }
 
+int mf_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups,
+                      void* stream) {
+  if (!src || !dst || bytes < 16 || bytes % 16 != 0 || workgroups < 1) return MF_EINVAL;
+  if (!a16(src) || !a16(dst)) return MF_EUNSUPPORTED;
+  mf::launch_probe_copy(src, dst, bytes, workgroups, S(stream));
+  return finish();
+}
+
 }  // extern "C"

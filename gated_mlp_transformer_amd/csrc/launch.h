@@ -111,5 +111,6 @@ void launch_dense_f32(const float* x, const float* w_gate, const float* w_up,
 void launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t s);
 void launch_probe_read(const void* src, int64_t bytes, int workgroups, uint32_t* out,
                        hipStream_t s);
+void launch_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t s);
 
 }  // namespace mf

@@ -6,6 +6,8 @@
 //  - mfma: every wave issues back-to-back v_mfma_f32_32x32x16_bf16 on 16
 //    independent accumulators (no loads, no LDS), one 256-thread workgroup per
 //    CU slot of the grid; FLOPs = waves * iters * 16 * 32*32*16*2.
+//  - copy: the same stream read and written to a second buffer; bytes =
+//    twice the buffer size.
 //  - read: a grid-strided stream of 16-byte loads over a buffer (each
 //    workgroup takes 32 KB runs), each lane folding what it read into one
 //    word that is stored once (so the loads are not dead); bytes = the buffer
@@ -65,7 +67,35 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
   out[static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x] = acc;
 }
 
+// dst = src, 16 bytes per access, each workgroup moving U consecutive 4 KB
+// runs per step (the read + write pattern of the normalisation and combine
+// kernels)
+__global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n16) {
+  constexpr int U = 4;
+  const int64_t span = static_cast<int64_t>(gridDim.x) * blockDim.x * U;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x * U + threadIdx.x; i < n16;
+       i += span) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * blockDim.x;
+      if (j < n16) v[u] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = i + static_cast<int64_t>(u) * blockDim.x;
+      if (j < n16) dst[j] = v[u];
+    }
+  }
+}
+
 }  // namespace
+
+void launch_probe_copy(const void* src, void* dst, int64_t bytes, int workgroups, hipStream_t s) {
+  probe_copy_kernel<<<workgroups, 256, 0, s>>>(static_cast<const u32x4*>(src),
+                                               static_cast<u32x4*>(dst), bytes / 16);
+}
 
 void launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t s) {
   probe_mfma_kernel<<<workgroups, 256, 0, s>>>(iters, out);

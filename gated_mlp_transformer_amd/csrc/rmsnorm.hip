@@ -148,8 +148,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 // 64 * 16 / sizeof(T)): no per-lane predicates (they compile to branches
 // around every load and store), no register prefetch of the next row, so the
 // kernel stays small and many waves per SIMD keep the loads in flight; one
-// row per wave at a time, gamma re-read from cache per row.
-template <typename T, int NV>
+// row per wave at a time, gamma re-read from cache per row. For few rows
+// (GPRE: latency, not bandwidth, decides) gamma's loads are issued with the
+// row's, so that they are not a second round trip after the sum; for many
+// rows they come after it, which keeps the kernel at fewer registers (more
+// waves per SIMD, more row loads in flight).
+template <typename T, int NV, bool GPRE>
 __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
                                                            T* y, int64_t rows, int d, float eps,
                                                            uint8_t* __restrict__ q,
@@ -160,9 +164,13 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
   for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; row < rows;
        row += stride) {
     const char* xr = reinterpret_cast<const char*>(x + row * d) + lane * 16;
-    u32x4 v[NV];
+    u32x4 v[NV], gv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = ld16(xr + i * kWave * 16);
+    if constexpr (GPRE) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) gv[i] = ld16(gr + i * kWave * 16);
+    }
     // sum of squares; the pairs are unpacked here by two ALU instructions the
     // compiler cannot merge with the output pass's unpacking, so that no
     // unpacked copy of the row stays in registers between the passes
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
     char* yr = reinterpret_cast<char*>(y + row * d) + lane * 16;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const u32x4 g = ld16(gr + i * kWave * 16);
+      const u32x4 g = GPRE ? gv[i] : ld16(gr + i * kWave * 16);
       u32x4 o;
       if constexpr (sizeof(T) == 2) {
         float f[8], gf[8], res[8];
@@ -229,15 +237,24 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
   auto* xp = static_cast<const T*>(x);
   auto* gp = static_cast<const T*>(gamma);
   auto* yp = static_cast<T*>(y);
+  if (rows <= 1024) {  // few rows: gamma with the row (one round trip)
+    switch (per_lane) {
+      case 1: rmsnorm_full_kernel<T, 1, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 2: rmsnorm_full_kernel<T, 2, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 4: rmsnorm_full_kernel<T, 4, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 8: rmsnorm_full_kernel<T, 8, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      default: break;  // wider rows: the kernels below
+    }
+  }
   switch (per_lane) {
-    case 1: rmsnorm_full_kernel<T, 1><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 2: rmsnorm_full_kernel<T, 2><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 4: rmsnorm_full_kernel<T, 4><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 8: rmsnorm_full_kernel<T, 8><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 16: rmsnorm_full_kernel<T, 16><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 1: rmsnorm_full_kernel<T, 1, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 2: rmsnorm_full_kernel<T, 2, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 4: rmsnorm_full_kernel<T, 4, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 8: rmsnorm_full_kernel<T, 8, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 16: rmsnorm_full_kernel<T, 16, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
     case 32:  // f32 rows of 8192
       if constexpr (sizeof(T) == 4) {
-        rmsnorm_full_kernel<T, 32><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs);
+        rmsnorm_full_kernel<T, 32, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs);
         return true;
       }
       return false;

@@ -431,11 +431,16 @@ int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s,
  * mf_probe_hbm_read - reads bytes (a multiple of 16) of src once, with
  *   grid-strided 16-byte loads from `workgroups` 256-thread workgroups; out
  *   [workgroups * 256] u32 receives one folded word per thread.
- * Both are asynchronous on `stream`; time them with events. MF_EINVAL on bad
+ * mf_probe_hbm_copy - copies bytes (a multiple of 16) from src to dst with
+ *   grid-strided 16-byte accesses from `workgroups` 256-thread workgroups:
+ *   HBM traffic = 2 * bytes, the read + write pattern of a streaming kernel.
+ * All are asynchronous on `stream`; time them with events. MF_EINVAL on bad
  * arguments.
  */
 int mf_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* out, void* stream);
 int mf_probe_hbm_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
+                      void* stream);
+int mf_probe_hbm_copy(const void* src, void* dst, int64_t bytes, int32_t workgroups,
                       void* stream);
 
 #ifdef __cplusplus
