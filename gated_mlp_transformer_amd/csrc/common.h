@@ -110,6 +110,23 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Buffer resource over [p, p + 2^31) for raw buffer loads: p must be the same
+// for every lane of the wave (it is read from the first lane), offsets are
+// bytes from p.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* p) {
+  const uint64_t u = static_cast<uint64_t>(reinterpret_cast<uintptr_t>(p));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  // 0x00020000: 32-bit data format, as raw buffer loads of dwords need
+  return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), 0x7fffffff, 0x00020000);
+}
+
+// 16 bytes at byte offset off of the buffer (default cache policy)
+__device__ __forceinline__ u32x4 ld16_buf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }

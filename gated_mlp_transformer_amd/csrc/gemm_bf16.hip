@@ -20,7 +20,8 @@
 // 128-row tiles. The router's split-K product uses MT = 4.
 //
 // Operand paths. A wave's weight fragments are private to it and come straight
-// from global memory into registers. The A tile is shared by the four waves
+// from global memory into registers (buffer loads: the row block's base in a
+// buffer resource, 32-bit lane offsets). The A tile is shared by the four waves
 // and goes through LDS (four stage buffers; 64-byte rows whose 16-byte chunks
 // are XOR-swizzled so that the 32-row fragment reads are bank-conflict free).
 // A moves two stages at a time, as whole 128-byte row segments (eight threads
@@ -148,12 +149,20 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
     for (int i = 0; i < NA; ++i)
       st16(&lds[(buf0 + (ld_c >> 2)) & 3][swz(ld_r + 32 * i, ld_c & 3)], areg[i]);
   };
+  // Weight fragments by buffer loads: the fragment row block's base in a
+  // buffer resource (scalar registers, the same for the whole wave) and a
+  // 32-bit per-lane offset (a row block spans K/16 fragments of 1 KB), in
+  // place of 64-bit per-lane addresses: measured 1-2 % faster (gate/up
+  // 432.7 -> 425 us at prefill).
+  __amdgpu_buffer_rsrc_t wrs[2];
+#pragma unroll
+  for (int jn = 0; jn < 2; ++jn) wrs[jn] = wave_rsrc(bp[jn] - lane * 16);
   auto load_b = [&](u32x4 (&br)[4], int kt) {
-    const int64_t kb = static_cast<int64_t>(kt) * (2 * FRAG);
+    const int kb = kt * (2 * FRAG);
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) br[jn * 2 + s] = ld16(bp[jn] + kb + s * FRAG);
+      for (int s = 0; s < 2; ++s) br[jn * 2 + s] = ld16_buf(wrs[jn], lane * 16 + kb + s * FRAG);
   };
   // One stage in a fixed instruction order. The k-step 0 fragments of every
   // live sub-tile are read from LDS first; the global loads (the weights of
