@@ -27,7 +27,7 @@ MF_F32, MF_BF16, MF_FP8_E4M3 = 0, 1, 2
 _lib.load()  # fail loudly at import if the HIP library is missing
 
 __all__ = [
-    "MoEFFNError", "PackedWeights", "pack_weights", "rmsnorm", "rmsnorm_quantize_fp8",
+    "MoEFFNError", "PackedWeights", "pack_weights", "pack_weights_kn", "rmsnorm", "rmsnorm_quantize_fp8",
     "moe_route_workspace_size",
     "moe_route",
     "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc", "moe_dispatch_masked", "MaskedDispatch",
@@ -162,6 +162,21 @@ def pack_weights(w: torch.Tensor, stream=None) -> PackedWeights:
     out = torch.empty(nbytes, dtype=torch.uint8, device=w3.device)
     _dev(w3, out)
     _ok("pack_weights", _lib.load().pack_weights(_p(w3), _p(out), G, N, K, code, _s(stream)))
+    return PackedWeights(out, w3.dtype, G, N, K)
+
+
+def pack_weights_kn(w: torch.Tensor, stream=None) -> PackedWeights:
+    """Pack w stored [groups, K, N] or [K, N] ([in, out], Y = X W): the same bytes as
+    pack_weights of its transpose."""
+    w3 = w.unsqueeze(0) if w.dim() == 2 else w
+    G, K, N = w3.shape
+    code = _dtype_code(w3.dtype)
+    nbytes = int(_lib.load().packed_weights_bytes(G, N, K, code))
+    if nbytes == 0:
+        raise ValueError(f"pack_weights_kn: unsupported shape/dtype {tuple(w3.shape)} {w3.dtype}")
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w3.device)
+    _dev(w3, out)
+    _ok("pack_weights_kn", _lib.load().pack_weights_kn(_p(w3), _p(out), G, N, K, code, _s(stream)))
     return PackedWeights(out, w3.dtype, G, N, K)
 
 

@@ -24,6 +24,7 @@ _SIGNATURES = {
                                     _i64, _i32, _f32, _c_void_p]),
     "packed_weights_bytes": (_size, [_i64, _i32, _i32, _i32]),
     "pack_weights": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p]),
+    "pack_weights_kn": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p]),
     "moe_route_workspace_size": (_size, [_i64, _i32, _i32]),
     "moe_route": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
                          _c_void_p, _c_void_p, _size, _c_void_p]),

@@ -83,12 +83,26 @@ int pack_weights(const void* src, void* dst, int64_t groups, int32_t N, int32_t 
   if (groups == 0) return MF_OK;
   if (!src || !dst) return MF_EINVAL;
   if (!a16(src) || !a16(dst)) return MF_EUNSUPPORTED;
-  mf::launch_pack(src, dst, groups, N, K, dtype == MF_FP8_E4M3, S(stream));
+  mf::launch_pack(src, dst, groups, N, K, dtype == MF_FP8_E4M3, false, S(stream));
+  return finish();
+}
+
+int pack_weights_kn(const void* src, void* dst, int64_t groups, int32_t N, int32_t K,
+                    int32_t dtype, void* stream) {
+  if (groups < 0 || N <= 0 || K <= 0) return MF_EINVAL;
+  if (dtype != MF_BF16 && dtype != MF_FP8_E4M3) return MF_EINVAL;
+  if ((dtype == MF_BF16 && K % 16 != 0) || (dtype == MF_FP8_E4M3 && K % 128 != 0))
+    return MF_EUNSUPPORTED;
+  if (groups == 0) return MF_OK;
+  if (!src || !dst) return MF_EINVAL;
+  if (!a16(dst) || (dtype == MF_BF16 && reinterpret_cast<uintptr_t>(src) % 2 != 0))
+    return MF_EUNSUPPORTED;
+  mf::launch_pack(src, dst, groups, N, K, dtype == MF_FP8_E4M3, true, S(stream));
   return finish();
 }
 
 size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E) {
-  if (T < 0 || d <= 0 || d % 256 != 0 || E < 8 || E > 256 || T > kI32Max / 8) return 0;
+  if (T < 0 || d <= 0 || d % 64 != 0 || E < 8 || E > 256 || T > kI32Max / 8) return 0;
   return mf::route_workspace_bytes(T, d, E);
 }
 
@@ -97,7 +111,7 @@ int moe_route(const void* x, const void* w_r, const float* bias, int64_t T, int3
               size_t workspace_bytes, void* stream) {
   if (!w_r || !bias || T < 0 || d <= 0) return MF_EINVAL;
   if (k <= 0 || E < k) return MF_EINVAL;
-  if (k != 8 || E > 256 || d % 256 != 0) return MF_EUNSUPPORTED;
+  if (k != 8 || E > 256 || d % 64 != 0) return MF_EUNSUPPORTED;
   if (T > kI32Max / 8) return MF_EUNSUPPORTED;
   if (T == 0) return MF_OK;  // zero-size buffers may be NULL
   if (!x || !topk_idx || !topk_w || !workspace) return MF_EINVAL;
@@ -190,8 +204,8 @@ int check_grouped(const void* a, const int32_t* offsets, int32_t e_count, int64_
   if (w_dtype != MF_BF16 && w_dtype != MF_FP8_E4M3) return MF_EINVAL;
   if (w_dtype == MF_FP8_E4M3 && (!s0 || !s1)) return MF_EINVAL;
   if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
-  if (w_dtype == MF_BF16 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
-  if (w_dtype == MF_FP8_E4M3 && (d % 256 != 0 || f % 256 != 0)) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_BF16 && (d % 64 != 0 || f % 64 != 0)) return MF_EUNSUPPORTED;
+  if (w_dtype == MF_FP8_E4M3 && (d % 128 != 0 || f % 128 != 0)) return MF_EUNSUPPORTED;
   if (max_rows == 0) {  // zero-size buffers may be NULL
     *empty = true;
     return MF_OK;
@@ -299,7 +313,7 @@ int check_a8(const void* a, const float* a_scale, const int32_t* offsets, int32_
   if (e_count < 1 || max_rows < 0 || K <= 0 || N <= 0) return MF_EINVAL;
   if (row_index && (src_rows < 1 || src_rows > kI32Max)) return MF_EINVAL;
   if (e_count > 256 || max_rows > kI32Max) return MF_EUNSUPPORTED;
-  if (K % 256 != 0 || N % 256 != 0) return MF_EUNSUPPORTED;
+  if (K % 128 != 0 || N % 128 != 0) return MF_EUNSUPPORTED;
   if (K > 16384) return MF_EUNSUPPORTED;  // weight-scale table of a tile: 128 slabs
   if (max_rows == 0) {  // zero-size buffers may be NULL
     *empty = true;
@@ -393,7 +407,7 @@ int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s, const 
   if (T > kI32Max) return MF_EUNSUPPORTED;
   if (T > 0 && (!x || !h_work || !partial)) return MF_EINVAL;  // NULL only if empty
   if (dtype == MF_BF16) {
-    if (d % 256 != 0 || f_s % 256 != 0) return MF_EUNSUPPORTED;
+    if (d % 64 != 0 || f_s % 64 != 0) return MF_EUNSUPPORTED;
     if (!a16(x) || !a16(w_gate_s) || !a16(w_up_s) || !a16(w_down_s) || !a16(h_work) ||
         !a16(partial))
       return MF_EUNSUPPORTED;

@@ -96,8 +96,11 @@ __device__ __forceinline__ i32x8 join(const u32x4& lo, const u32x4& hi) {
 // LDS buffer; barrier. Every scale is consumed together with the data it
 // travels with, so the one in-order load counter never holds a weight
 // prefetch back for a scale, and the four-stage loop body has no branches
-// (a two-stage tail takes nk % 4 == 2), so every wait is static.
-template <int MT, int NM, bool GATED>
+// (a two-stage tail takes nk % 4 == 2; with ODD, for an odd slab count, a
+// tail of one or three stages, in a separate kernel so that the common even
+// case keeps its register allocation), so every wait inside the loop is
+// static.
+template <int MT, int NM, bool GATED, bool ODD>
 __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* const (&ap)[MT],
                                           const float* const (&aspr)[MT],
                                           const uint8_t* const (&bp)[2], const float* s_sw,
@@ -180,14 +183,22 @@ __device__ __forceinline__ void a8_k_loop(f32x16 (&acc)[MT][2], const uint8_t* c
     MF_A8_STEP(2)
     MF_A8_STEP(3)
   }
-  if (kt < nk) {  // nk is even: two stages left
-    MF_A8_STEP(0)
-    MF_A8_STEP(1)
+  // the last nk % 4 stages, in the slots and buffers the four-stage body
+  // would have used
+  if constexpr (!ODD) {
+    if (kt < nk) {  // nk is even: two stages left
+      MF_A8_STEP(0)
+      MF_A8_STEP(1)
+    }
+  } else {
+    if (kt < nk) MF_A8_STEP(0)
+    if (kt + 1 < nk) MF_A8_STEP(1)
+    if (kt + 2 < nk) MF_A8_STEP(2)
   }
 #undef MF_A8_STEP
 }
 
-template <int MT, bool GATED>
+template <int MT, bool GATED, bool ODD>
 __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
   constexpr int BN_OUT = GATED ? 128 : 256;
   __shared__ __attribute__((aligned(16))) char lds[2][MT * 32 * ROW8];
@@ -198,7 +209,9 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
   __shared__ int s_end[MAXG];
 
   const int tid = threadIdx.x;
-  const int NT = p.N * (GATED ? 2 : 1) / 256;   // n-tiles of 256 weight rows
+  // n-tiles of 256 weight rows (gated: 128 gate + 128 up; N % 128 == 0); the
+  // down GEMM's last n-tile may hold only 128 valid rows
+  const int NT = GATED ? p.N / 128 : (p.N + 255) / 256;
   const int KB = p.K / 128;
   const int NB16 = p.N / 16;
   const int NB128 = p.N / 128;
@@ -298,10 +311,10 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
     static_assert(MT == 4, "one tile height");
     {
       switch (nm) {
-        case 1: a8_k_loop<MT, 1, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
-        case 2: a8_k_loop<MT, 2, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
-        case 3: a8_k_loop<MT, 3, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
-        default: a8_k_loop<MT, 4, GATED>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        case 1: a8_k_loop<MT, 1, GATED, ODD>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        case 2: a8_k_loop<MT, 2, GATED, ODD>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        case 3: a8_k_loop<MT, 3, GATED, ODD>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
+        default: a8_k_loop<MT, 4, GATED, ODD>(acc, ap, aspr, bp, s_sw[wave], lds, s_sa, nk, sstride, ld_r, ld_c, lane); break;
       }
     }
 
@@ -326,6 +339,7 @@ __global__ __launch_bounds__(256, 1) void gemm_a8_kernel(A8Params p) {
 #pragma unroll
           for (int jn = 0; jn < 2; ++jn) {
             const int col = n0 + wave * 64 + jn * 32 + 8 * qq + 4 * lg;
+            if (col >= p.N) continue;  // past a partial last n-tile
             *reinterpret_cast<u32x2*>(p.c + (grow * p.ldc + col) * 2) =
                 u32x2{pack_bf16x2(acc[i][jn][4 * qq], acc[i][jn][4 * qq + 1]),
                       pack_bf16x2(acc[i][jn][4 * qq + 2], acc[i][jn][4 * qq + 3])};
@@ -359,8 +373,9 @@ void launch_gemm_gateup_a8(const void* a, const float* a_scale, const int32_t* a
   A8Params p{static_cast<const uint8_t*>(a), a_scale, a_rows, static_cast<int>(a_src_rows),
              static_cast<const uint8_t*>(w_gate), static_cast<const uint8_t*>(w_up), s_gate, s_up,
              static_cast<char*>(h), offsets, e_count, static_cast<int>(max_rows), K, N, N};
-  const int grid = a8_grid(max_rows, e_count, N * 2 / 256, num_cus);
-  gemm_a8_kernel<MT_A8, true><<<grid, 256, 0, s>>>(p);
+  const int grid = a8_grid(max_rows, e_count, N / 128, num_cus);
+  if ((K / 128) % 2) gemm_a8_kernel<MT_A8, true, true><<<grid, 256, 0, s>>>(p);
+  else gemm_a8_kernel<MT_A8, true, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_a8(const void* a, const float* a_scale, const int32_t* offsets,
@@ -369,8 +384,9 @@ void launch_gemm_down_a8(const void* a, const float* a_scale, const int32_t* off
   A8Params p{static_cast<const uint8_t*>(a), a_scale, nullptr, 0,
              static_cast<const uint8_t*>(w_down), nullptr, s_down, nullptr,
              static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N, N};
-  const int grid = a8_grid(max_rows, e_count, N / 256, num_cus);
-  gemm_a8_kernel<MT_A8, false><<<grid, 256, 0, s>>>(p);
+  const int grid = a8_grid(max_rows, e_count, (N + 255) / 256, num_cus);
+  if ((K / 128) % 2) gemm_a8_kernel<MT_A8, false, true><<<grid, 256, 0, s>>>(p);
+  else gemm_a8_kernel<MT_A8, false, false><<<grid, 256, 0, s>>>(p);
 }
 
 }  // namespace mf

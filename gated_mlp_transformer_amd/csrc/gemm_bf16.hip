@@ -117,7 +117,9 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f
 
 }  // namespace
 
-// K loop of one tile for NM live 32-row sub-tiles (1..MT). Branch-free: the
+// K loop of one tile for NM live 32-row sub-tiles (1..MT); nk (stages of 32)
+// is a multiple of 4, or with TAIL of 2 but not 4 (a separate kernel: a tail
+// in the same code made the compiler spill inside the MFMA loop). Branch-free: the
 // prefetch stage indices are clamped (the last steps re-load the final stage),
 // so the compiler's vmcnt waits track exactly the loads being consumed.
 //
@@ -125,7 +127,7 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f
 // the MFMAs of t; (t odd) write the A pair loaded at stage t-1 into its two
 // LDS buffers; barrier. Thread (ld_r, ld_c) moves 16-byte chunk ld_c of the
 // 128-byte pair segment of rows ld_r + 32i, i < NM.
-template <int MT, int NM>
+template <int MT, int NM, bool TAIL>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
                                        const int (&arow)[MT], int64_t Kb,
                                        const char* const (&bp)[2],
@@ -232,16 +234,21 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
           min(t_ + PREF, nk - 1));                                                         \
     __syncthreads();                                                                       \
   }
-  for (int kt = 0; kt < nk; kt += SLOTS) {
+  int kt = 0;
+  for (; TAIL ? kt + SLOTS <= nk : kt < nk; kt += SLOTS) {
     MF_GEMM_STEP(0)
     MF_GEMM_STEP(1)
     MF_GEMM_STEP(2)
     MF_GEMM_STEP(3)
   }
+  if constexpr (TAIL) {  // nk % 4 == 2: one stage pair left, in slots 0 and 1
+    MF_GEMM_STEP(0)
+    MF_GEMM_STEP(1)
+  }
 #undef MF_GEMM_STEP
 }
 
-template <int MT, bool GATED, bool OUT_F32>
+template <int MT, bool GATED, bool OUT_F32, bool TAIL>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   constexpr int BM = MT * 32;
   constexpr int BN_OUT = GATED ? 128 : 256;
@@ -352,22 +359,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     __syncthreads();  // the previous tile's LDS reads are done
     if constexpr (MT == 8) {
       switch (nm) {
-        case 1: k_loop<MT, 1>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 2: k_loop<MT, 2>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 3: k_loop<MT, 3>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 4: k_loop<MT, 4>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 5: k_loop<MT, 5>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 6: k_loop<MT, 6>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 7: k_loop<MT, 7>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        default: k_loop<MT, 8>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 1: k_loop<MT, 1, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 4: k_loop<MT, 4, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 5: k_loop<MT, 5, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 6: k_loop<MT, 6, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 7: k_loop<MT, 7, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 8, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
       }
     } else {
       static_assert(MT == 4, "MT is 4 or 8");
       switch (nm) {
-        case 1: k_loop<MT, 1>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 2: k_loop<MT, 2>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        case 3: k_loop<MT, 3>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
-        default: k_loop<MT, 4>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 1: k_loop<MT, 1, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 2: k_loop<MT, 2, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        case 3: k_loop<MT, 3, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
+        default: k_loop<MT, 4, TAIL>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane); break;
       }
     }
 
@@ -383,6 +390,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
       for (int q = 0; q < 4; ++q) {
         if constexpr (GATED) {
           const int col = n0 + wave * 32 + 8 * q + 4 * lg;
+          if (col >= p.n_valid) continue;  // n_valid % 32 == 0: whole 4-column groups
           float h[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) h[r] = siluf_(acc[i][0][4 * q + r]) * acc[i][1][4 * q + r];
@@ -427,6 +435,10 @@ namespace {
 constexpr int MT_GROUPED = 8;  // 256-row tiles for the grouped and dense GEMMs
 constexpr int MT_SPLITK = 4;   // 128-row tiles for the router's split-K product
 
+// A contraction of K % 128 == 64 (a multiple of 64 but not of the four-stage
+// loop body) takes the kernels with the two-stage tail.
+bool tail_stages(int kc) { return (kc / BK) % SLOTS != 0; }
+
 // Persistent grid: at most one workgroup per CU, a multiple of 8 (the XCD
 // count), and no more than an upper bound on the tiles. With offsets each
 // group can add one partial m-tile; a single dense group (offsets == nullptr)
@@ -451,8 +463,10 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
                static_cast<int>(max_rows), K, N / 32, N, N, K, 0, counts, cap};
   const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
-                                   offsets == nullptr && counts == nullptr, N / 128, num_cus);
-  gemm_bf16_kernel<MT_GROUPED, true, false><<<grid, 256, 0, s>>>(p);
+                                   offsets == nullptr && counts == nullptr, (N + 127) / 128,
+                                   num_cus);
+  if (tail_stages(K)) gemm_bf16_kernel<MT_GROUPED, true, false, true><<<grid, 256, 0, s>>>(p);
+  else gemm_bf16_kernel<MT_GROUPED, true, false, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
@@ -462,11 +476,16 @@ void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, i
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
                N, N, K, 0, counts, cap};
   const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
-                                   offsets == nullptr && counts == nullptr, N / 256, num_cus);
-  if (out_f32)
-    gemm_bf16_kernel<MT_GROUPED, false, true><<<grid, 256, 0, s>>>(p);
-  else
-    gemm_bf16_kernel<MT_GROUPED, false, false><<<grid, 256, 0, s>>>(p);
+                                   offsets == nullptr && counts == nullptr, (N + 255) / 256,
+                                   num_cus);
+  const bool tail = tail_stages(K);
+  if (out_f32) {
+    if (tail) gemm_bf16_kernel<MT_GROUPED, false, true, true><<<grid, 256, 0, s>>>(p);
+    else gemm_bf16_kernel<MT_GROUPED, false, true, false><<<grid, 256, 0, s>>>(p);
+  } else {
+    if (tail) gemm_bf16_kernel<MT_GROUPED, false, false, true><<<grid, 256, 0, s>>>(p);
+    else gemm_bf16_kernel<MT_GROUPED, false, false, false><<<grid, 256, 0, s>>>(p);
+  }
 }
 
 void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b, int n_valid,
@@ -480,7 +499,10 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
                rows * static_cast<int64_t>(n_valid)};
   // splits x tiles workgroups: size x so that all of them fit in one round
   int gx = persistent_grid(rows, MT_SPLITK * 32, 1, true, 1, num_cus / splits);
-  gemm_bf16_kernel<MT_SPLITK, false, true><<<dim3(gx, splits), 256, 0, s>>>(p);
+  if (tail_stages(K / splits))
+    gemm_bf16_kernel<MT_SPLITK, false, true, true><<<dim3(gx, splits), 256, 0, s>>>(p);
+  else
+    gemm_bf16_kernel<MT_SPLITK, false, true, false><<<dim3(gx, splits), 256, 0, s>>>(p);
 }
 
 }  // namespace mf

@@ -72,7 +72,7 @@ struct SlabRegs {
 
 }  // namespace
 
-template <bool GATED>
+template <bool GATED, bool ODD>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
   constexpr int NTW = GATED ? 256 : 512;  // output columns per work item
   constexpr int QH = GATED ? R / 2 : R;   // sub-tiles per weight matrix per wave
@@ -197,8 +197,10 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
       };
 
       // Two register sets in turn; the next slab's loads are issued before
-      // the current slab is consumed. Slab counts are even (K % 256 == 0) and
-      // the last pair is peeled, so every wait in the loop is static.
+      // the current slab is consumed. The last two slabs of a chunk are
+      // peeled (with ODD, for an odd slab count, a separate kernel: the branch
+      // raised the even case from 252 to 308 VGPRs, one wave per SIMD), so
+      // every wait inside the loop is static.
       // (A scheduling barrier after each group of loads keeps the compiler
       // from sinking them below the MFMAs they are meant to run under.)
       SlabRegs<R> r0, r1;
@@ -219,10 +221,14 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
           __builtin_amdgcn_sched_barrier(0);
           compute(r1, j + 1);
         }
-        load(r1, kc + j + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(r0, j);
-        compute(r1, j + 1);
+        if (!ODD || j + 1 < nks) {
+          load(r1, kc + j + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(r0, j);
+          compute(r1, j + 1);
+        } else {  // an odd slab count (K % 256 == 128): one slab left
+          compute(r0, j);
+        }
       }
 
       // lane holds output columns 4*lg..4*lg+3 of sub-tile q for row lr.
@@ -263,7 +269,9 @@ void launch_gemm_gateup_fp8(const void* a, const int32_t* a_rows, int64_t a_src_
               static_cast<const uint8_t*>(w_gate),
               static_cast<const uint8_t*>(w_up), s_gate, s_up, static_cast<char*>(h), offsets,
               e_count, static_cast<int>(max_rows), K, N, counts, cap};
-  gemm_fp8_kernel<true><<<dim3(fp8_grid(e_count, N, 256, num_cus)), 256, 0, s>>>(p);
+  const dim3 grid(fp8_grid(e_count, N, 256, num_cus));
+  if ((K / SLAB) % 2) gemm_fp8_kernel<true, true><<<grid, 256, 0, s>>>(p);
+  else gemm_fp8_kernel<true, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
@@ -272,7 +280,9 @@ void launch_gemm_down_fp8(const void* a, const int32_t* offsets, int e_count, in
   Fp8Params p{static_cast<const char*>(a), nullptr, 0, static_cast<const uint8_t*>(w_down), nullptr, s_down,
               nullptr, static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N,
               counts, cap};
-  gemm_fp8_kernel<false><<<dim3(fp8_grid(e_count, N, 512, num_cus)), 256, 0, s>>>(p);
+  const dim3 grid(fp8_grid(e_count, N, 512, num_cus));
+  if ((K / SLAB) % 2) gemm_fp8_kernel<false, true><<<grid, 256, 0, s>>>(p);
+  else gemm_fp8_kernel<false, false><<<grid, 256, 0, s>>>(p);
 }
 
 }  // namespace mf

@@ -93,8 +93,10 @@ __device__ __forceinline__ u32x4 codes_to_bf16(const u32x4& lo, const u32x4& hi,
 // fragments' codes and run two MFMAs per live sub-tile into the block
 // partials; add the partials into the result with the block's weight scales;
 // write A(t+1) to the other LDS buffer; barrier. The two-stage loop body has
-// no branches (nk is even), so every wait is static.
-template <int NM, bool GATED>
+// no branches (an odd slab count takes a one-stage tail, in a separate kernel
+// so that the even case keeps its register allocation), so every wait inside
+// the loop is static.
+template <int NM, bool GATED, bool ODD>
 __device__ __forceinline__ void w8_k_loop(f32x16 (&acc)[MT][2], const char* abase,
                                           const int (&arow)[2 * MT], int64_t Kb,
                                           const uint8_t* const (&bp)[2], const float* s_sw,
@@ -168,14 +170,16 @@ __device__ __forceinline__ void w8_k_loop(f32x16 (&acc)[MT][2], const char* abas
           min(t_ + WSLOTS - 1, nk - 1));                                                   \
     __syncthreads();                                                                       \
   }
-  for (int kt = 0; kt < nk; kt += WSLOTS) {  // nk is even
+  int kt = 0;
+  for (; ODD ? kt + WSLOTS <= nk : kt < nk; kt += WSLOTS) {
     MF_W8_STEP(0)
     MF_W8_STEP(1)
   }
+  if constexpr (ODD) MF_W8_STEP(0)  // an odd slab count: the last slab
 #undef MF_W8_STEP
 }
 
-template <bool GATED>
+template <bool GATED, bool ODD>
 __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
   constexpr int BN_OUT = GATED ? 128 : 256;
   __shared__ __attribute__((aligned(16))) char lds[2][MT * 32 * ROWW];
@@ -185,7 +189,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
   __shared__ int s_end[MAXG];
 
   const int tid = threadIdx.x;
-  const int NT = p.N * (GATED ? 2 : 1) / 256;   // n-tiles of 256 weight rows
+  // n-tiles of 256 weight rows (gated: 128 gate + 128 up; N % 128 == 0); the
+  // down GEMM's last n-tile may hold only 128 valid rows
+  const int NT = GATED ? p.N / 128 : (p.N + 255) / 256;
   const int KB = p.K / 128;
   const int NB16 = p.N / 16;
   const int NB128 = p.N / 128;
@@ -280,10 +286,10 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
       s_sw[wave][KB + j] = wsp[1][j];
     }
     switch (nm) {
-      case 1: w8_k_loop<1, GATED>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
-      case 2: w8_k_loop<2, GATED>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
-      case 3: w8_k_loop<3, GATED>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
-      default: w8_k_loop<4, GATED>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
+      case 1: w8_k_loop<1, GATED, ODD>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
+      case 2: w8_k_loop<2, GATED, ODD>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
+      case 3: w8_k_loop<3, GATED, ODD>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
+      default: w8_k_loop<4, GATED, ODD>(acc, abase, arow, Kb, bp, s_sw[wave], lds, nk, sstride, ld_r, ld_c, lane); break;
     }
 
     // epilogue: lane l holds, for token row lr of sub-tile i, output columns
@@ -307,6 +313,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
 #pragma unroll
           for (int jn = 0; jn < 2; ++jn) {
             const int col = n0 + wave * 64 + jn * 32 + 8 * qq + 4 * lg;
+            if (col >= p.N) continue;  // past a partial last n-tile
             *reinterpret_cast<u32x2*>(p.c + (grow * p.N + col) * 2) =
                 u32x2{pack_bf16x2(acc[i][jn][4 * qq], acc[i][jn][4 * qq + 1]),
                       pack_bf16x2(acc[i][jn][4 * qq + 2], acc[i][jn][4 * qq + 3])};
@@ -343,7 +350,9 @@ void launch_gemm_gateup_w8(const void* a, const int32_t* a_rows, int64_t a_src_r
   W8Params p{static_cast<const char*>(a), a_rows, static_cast<int>(a_src_rows),
              static_cast<const uint8_t*>(w_gate), static_cast<const uint8_t*>(w_up), s_gate, s_up,
              static_cast<char*>(h), offsets, e_count, static_cast<int>(max_rows), K, N};
-  gemm_w8_kernel<true><<<w8_grid(max_rows, e_count, N * 2 / 256, num_cus), 256, 0, s>>>(p);
+  const int grid = w8_grid(max_rows, e_count, N / 128, num_cus);
+  if ((K / 128) % 2) gemm_w8_kernel<true, true><<<grid, 256, 0, s>>>(p);
+  else gemm_w8_kernel<true, false><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_w8(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
@@ -352,7 +361,9 @@ void launch_gemm_down_w8(const void* a, const int32_t* offsets, int e_count, int
   W8Params p{static_cast<const char*>(a), nullptr, 0, static_cast<const uint8_t*>(w_down),
              nullptr, s_down, nullptr, static_cast<char*>(y), offsets, e_count,
              static_cast<int>(max_rows), K, N};
-  gemm_w8_kernel<false><<<w8_grid(max_rows, e_count, N / 256, num_cus), 256, 0, s>>>(p);
+  const int grid = w8_grid(max_rows, e_count, (N + 255) / 256, num_cus);
+  if ((K / 128) % 2) gemm_w8_kernel<false, true><<<grid, 256, 0, s>>>(p);
+  else gemm_w8_kernel<false, false><<<grid, 256, 0, s>>>(p);
 }
 
 }  // namespace mf

@@ -40,7 +40,8 @@ void launch_dispatch_masked(const int32_t* idx, int64_t T, int k, int e_begin, i
 
 // Weight packing into MFMA fragment order (pack.hip).
 size_t packed_bytes(int64_t groups, int N, int K, bool fp8);
-void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8,
+// kn: src is [groups, K, N] instead of [groups, N, K]; the output is the same.
+void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8, bool kn,
                  hipStream_t s);
 
 // bf16 MFMA grouped GEMMs on packed weights. offsets == nullptr means one group
@@ -56,7 +57,7 @@ void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count,
                            const int32_t* counts = nullptr, int cap = 0);
 
 // C_y = A[:, y*K/splits : (y+1)*K/splits] B[:n_valid, same]^T in fp32 for each K
-// split y (one group, bf16 operands). Requires (K / splits) % 256 == 0.
+// split y (one group, bf16 operands). Requires (K / splits) % 64 == 0.
 void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b, int n_valid,
                                int splits, float* c_partials, int num_cus, hipStream_t s);
 

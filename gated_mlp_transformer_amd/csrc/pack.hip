@@ -17,6 +17,12 @@
 //   load-only probe of the decode pattern).
 //
 // A pure permutation (plus zero padding): one thread moves one 16-byte chunk.
+//
+// The source may also be given [groups, K, N] ([in, out], the Y = X W
+// orientation of the pages' gated-MLP formula): the packed result is the same
+// as for its transpose. Then a chunk's 8 (bf16) or 16 (fp8) elements lie N
+// apart in the source and are gathered one by one; neighbouring lanes take
+// neighbouring rows, i.e. neighbouring source addresses.
 #include "common.h"
 #include "launch.h"
 
@@ -42,7 +48,7 @@ size_t packed_bytes(int64_t groups, int N, int K, bool fp8) {
   return static_cast<size_t>(groups) * nb * g.rows_blk * K * g.esize;
 }
 
-template <bool FP8>
+template <bool FP8, bool KN>
 __global__ __launch_bounds__(256) void pack_kernel(const char* __restrict__ src, char* __restrict__ dst,
                                                    int64_t groups, int N, int K) {
   const PackGeom g = geom(FP8);
@@ -82,12 +88,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const char* __restrict__ src,
       col = static_cast<int64_t>(kb) * 16 + 8 * (lane / 32);
     }
     u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (row < N) v = ld16(src + ((grp * N + row) * K + col) * g.esize);
+    if (row < N) {
+      if constexpr (!KN) {
+        v = ld16(src + ((grp * N + row) * K + col) * g.esize);
+      } else {
+        // element col + i of row `row`: src[grp][col + i][row]
+        const int64_t base = (grp * K + col) * N + row;
+        if constexpr (FP8) {
+          const uint8_t* s8 = reinterpret_cast<const uint8_t*>(src);
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            v[i / 4] |= static_cast<uint32_t>(s8[base + static_cast<int64_t>(i) * N]) << (8 * (i % 4));
+        } else {
+          const uint16_t* s16 = reinterpret_cast<const uint16_t*>(src);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            v[i / 2] |= static_cast<uint32_t>(s16[base + static_cast<int64_t>(i) * N]) << (16 * (i % 2));
+        }
+      }
+    }
     st16(dst + c * 16, v);
   }
 }
 
-void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8,
+void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool fp8, bool kn,
                  hipStream_t s) {
   const PackGeom g = geom(fp8);
   const int64_t nb = (N + g.rows_blk - 1) / g.rows_blk;
@@ -95,12 +119,16 @@ void launch_pack(const void* src, void* dst, int64_t groups, int N, int K, bool 
   int64_t grid = (chunks + 255) / 256;
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
-  if (fp8)
-    pack_kernel<true><<<dim3(static_cast<unsigned>(grid)), 256, 0, s>>>(
-        static_cast<const char*>(src), static_cast<char*>(dst), groups, N, K);
-  else
-    pack_kernel<false><<<dim3(static_cast<unsigned>(grid)), 256, 0, s>>>(
-        static_cast<const char*>(src), static_cast<char*>(dst), groups, N, K);
+  const dim3 gr(static_cast<unsigned>(grid));
+  const char* sp = static_cast<const char*>(src);
+  char* dp = static_cast<char*>(dst);
+  if (fp8) {
+    if (kn) pack_kernel<true, true><<<gr, 256, 0, s>>>(sp, dp, groups, N, K);
+    else pack_kernel<true, false><<<gr, 256, 0, s>>>(sp, dp, groups, N, K);
+  } else {
+    if (kn) pack_kernel<false, true><<<gr, 256, 0, s>>>(sp, dp, groups, N, K);
+    else pack_kernel<false, false><<<gr, 256, 0, s>>>(sp, dp, groups, N, K);
+  }
 }
 
 }  // namespace mf

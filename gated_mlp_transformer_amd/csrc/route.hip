@@ -88,8 +88,8 @@ int route_splits(int64_t T, int d) {
     return ks;
   }
   const int64_t tiles = (T + kTokTile - 1) / kTokTile;
-  // each split's K range must stay a multiple of 256
-  while ((d / 256) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs && ks * 2 <= kMaxSplits) ks *= 2;
+  // each split's K range must stay a multiple of 64 (the GEMM's stage pair)
+  while ((d / 64) % (ks * 2) == 0 && tiles * ks * 2 <= kTargetWGs && ks * 2 <= kMaxSplits) ks *= 2;
   return ks;
 }
 

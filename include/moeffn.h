@@ -116,6 +116,20 @@ int pack_weights(const void* src, void* dst, int64_t groups, int32_t N, int32_t 
                  int32_t dtype, void* stream);
 
 /*
+ * pack_weights_kn - pack_weights for weights stored [groups, K, N] ([in, out],
+ * row-major: the orientation of a linear layer W in R^{d x f} with Y = X W in
+ * "推理计算流梳理", 张量并行和通信, used by the gated MLP of 实际 MLP 计算策略,
+ * so W_gate and W_up of an expert are [d, f] and W_down [f, d]). dst
+ * receives exactly the bytes pack_weights
+ * writes for the transposed [groups, N, K] tensor; N, K, dtype, the size of
+ * dst and the requirements are the same. The source is read element by
+ * element (bf16: src 2-byte aligned; dst 16-byte aligned). Errors: as
+ * pack_weights.
+ */
+int pack_weights_kn(const void* src, void* dst, int64_t groups, int32_t N, int32_t K,
+                    int32_t dtype, void* stream);
+
+/*
  * moe_route_workspace_size - bytes of device workspace moe_route needs for
  * T tokens, hidden size d and E experts (fp32 partial logits). Depends on
  * (T, d, E) only. Returns 0 for arguments moe_route would reject.
@@ -141,7 +155,7 @@ size_t moe_route_workspace_size(int64_t T, int32_t d, int32_t E);
  * contraction may be split into ranges whose fp32 partial sums are added in a
  * fixed order); s, s + b and w are fp32. The result is the same run to run.
  * Ties in s + b go to the lower id.
- * Requires k == 8, 8 <= E <= 256, d % 256 == 0.
+ * Requires k == 8, 8 <= E <= 256, d % 64 == 0.
  */
 int moe_route(const void* x, const void* w_r, const float* bias, int64_t T,
               int32_t d, int32_t E, int32_t k, int32_t* topk_idx, float* topk_w,
@@ -264,8 +278,8 @@ int moe_dispatch_masked(const int32_t* topk_idx, int64_t T, int32_t k, int32_t e
  * the work is tiled 128 rows at a time when max_rows >= 32 * e_count (and
  * d, f <= 16384), else 16 rows per pass over each expert's weights (decode
  * shapes, where an expert holds a few rows).
- * Requires 1 <= e_count <= 256; bf16: d % 256 == 0 and f % 256 == 0;
- * fp8: d % 256 == 0 and f % 256 == 0.
+ * Requires 1 <= e_count <= 256; bf16: d % 64 == 0 and f % 64 == 0;
+ * fp8: d % 128 == 0 and f % 128 == 0.
  */
 int grouped_swiglu(const void* x, const int32_t* row_index, int64_t src_rows,
                    const int32_t* offsets, int32_t e_count, int64_t max_rows, int32_t d,
@@ -352,7 +366,7 @@ int quantize_fp8_rows(const void* x, int64_t rows, const int32_t* row_count, int
  * Each 128-deep block of the contraction is summed exactly on the fp8 MFMA
  * (fp32 accumulation) and added into the fp32 result scaled by its activation
  * and weight scales; SiLU(g)*u in fp32 in the epilogue.
- * Requires 1 <= e_count <= 256, d % 256 == 0, f % 256 == 0, d <= 16384
+ * Requires 1 <= e_count <= 256, d % 128 == 0, f % 128 == 0, d <= 16384
  * (MF_EUNSUPPORTED otherwise).
  */
 int grouped_gate_up_a8(const void* xq, const float* x_scale, const int32_t* row_index,
@@ -412,7 +426,7 @@ int moe_combine(const void* y_perm, const int32_t* inv_pos, const float* topk_w,
  * h_work   [T, f_s]  dtype, out: H_i
  * partial  [T, d]    f32, out: P_i, the full-shape partial sum
  * dtype MF_BF16 (MFMA, fp32 accumulation; H_i rounded to bf16; requires
- * d % 256 == 0, f_s % 256 == 0) or MF_F32 (fp32 FMA throughout; any sizes).
+ * d % 64 == 0, f_s % 64 == 0) or MF_F32 (fp32 FMA throughout; any sizes).
  */
 int tp_shard_mlp(const void* x, const void* w_gate_s, const void* w_up_s,
                  const void* w_down_s, int64_t T, int32_t d, int32_t f_s,

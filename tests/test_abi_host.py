@@ -93,11 +93,20 @@ def test_pack_validation(lib):
     assert lib.pack_weights(P, P, 1, 32, 64, F32, N) == MF_EINVAL
     assert lib.pack_weights(P, P, 1, 32, 40, BF16, N) == MF_EUNSUPPORTED
     assert lib.pack_weights(N, N, 0, 32, 64, BF16, N) == MF_OK
+    # [in, out] sources: the same rules; bf16 sources need 2-byte alignment only
+    assert lib.pack_weights_kn(N, P, 1, 32, 64, BF16, N) == MF_EINVAL
+    assert lib.pack_weights_kn(P, P, 1, 32, 64, F32, N) == MF_EINVAL
+    assert lib.pack_weights_kn(P, P, 1, 32, 40, BF16, N) == MF_EUNSUPPORTED
+    assert lib.pack_weights_kn(P, P, 1, 32, 192, FP8, N) == MF_EUNSUPPORTED
+    assert lib.pack_weights_kn(ctypes.c_void_p(0x100001), P, 1, 32, 64, BF16, N) == MF_EUNSUPPORTED
+    assert lib.pack_weights_kn(P, ctypes.c_void_p(0x100008), 1, 32, 64, BF16, N) == MF_EUNSUPPORTED
+    assert lib.pack_weights_kn(N, N, 0, 32, 64, BF16, N) == MF_OK
 
 
 def test_route_validation(lib):
     ws = lib.moe_route_workspace_size(4, 256, 256)
-    assert ws > 0 and lib.moe_route_workspace_size(4, 64, 256) == 0
+    assert ws > 0 and lib.moe_route_workspace_size(4, 64, 256) > 0
+    assert lib.moe_route_workspace_size(4, 96, 256) == 0
     call = lambda x=P, b=P, T=4, d=256, E=256, k=8, wsp=P, wsb=ws: lib.moe_route(  # noqa: E731
         x, P, b, T, d, E, k, P, P, wsp, wsb, N)
     assert call(b=N) == MF_EINVAL
@@ -107,13 +116,16 @@ def test_route_validation(lib):
     assert call(wsb=ws - 4) == MF_EINVAL
     assert call(k=6) == MF_EUNSUPPORTED           # k != 8
     assert call(E=257) == MF_EUNSUPPORTED
-    assert call(d=64) == MF_EUNSUPPORTED          # d % 256
+    assert call(d=96) == MF_EUNSUPPORTED          # d % 64
     assert call(T=0, x=N, wsp=N, wsb=0) == MF_OK
     # few tokens: (T/32) x 8 x splits workgroups, K ranges multiples of 64
     assert lib.moe_route_workspace_size(256, 4096, 256) == 4 * 256 * 256 * 4
     assert lib.moe_route_workspace_size(64, 4096, 256) == 16 * 64 * 256 * 4
     # many tokens: 128-token tiles x splits <= 256 workgroups
     assert lib.moe_route_workspace_size(4096, 4096, 256) == 8 * 4096 * 256 * 4
+    # K ranges stay multiples of 64: d = 4160 = 65 * 64 takes no split
+    assert lib.moe_route_workspace_size(4096, 4160, 256) == 4096 * 256 * 4
+    assert lib.moe_route_workspace_size(4096, 4224, 256) == 2 * 4096 * 256 * 4
 
 
 def test_permute_validation(lib):
@@ -146,10 +158,12 @@ def test_grouped_swiglu_validation(lib):
     assert call(ec=0) == MF_EINVAL
     assert call(wdt=F32) == MF_EINVAL
     assert call(wdt=FP8) == MF_EINVAL                      # fp8 needs scales
-    assert call(d=128) == MF_EUNSUPPORTED                  # bf16 needs d % 256
-    assert call(f=64) == MF_EUNSUPPORTED                   # bf16 needs f % 256
-    assert call(f=384) == MF_EUNSUPPORTED
-    assert call(wdt=FP8, s=(P, P, P), f=384) == MF_EUNSUPPORTED   # fp8 needs f % 256
+    assert call(d=96) == MF_EUNSUPPORTED                   # bf16 needs d % 64
+    assert call(f=32) == MF_EUNSUPPORTED                   # bf16 needs f % 64
+    assert call(d=192, f=320, rows=0) == MF_OK
+    assert call(wdt=FP8, s=(P, P, P), f=320) == MF_EUNSUPPORTED   # fp8 needs f % 128
+    assert call(wdt=FP8, s=(P, P, P), d=192) == MF_EUNSUPPORTED   # fp8 needs d % 128
+    assert call(wdt=FP8, s=(P, P, P), d=384, f=640, rows=0) == MF_OK
     assert call(ec=300) == MF_EUNSUPPORTED
     assert call(rows=0) == MF_OK
 
@@ -163,8 +177,9 @@ def test_combine_and_shard_validation(lib):
         == MF_EUNSUPPORTED                                 # misaligned residual
     assert lib.moe_combine(P, P, P, 0, 8, 64, 32, N, P, BF16, N) == MF_OK
     assert lib.tp_shard_mlp(P, P, P, N, 4, 256, 256, BF16, P, P, N) == MF_EINVAL
-    assert lib.tp_shard_mlp(P, P, P, P, 4, 192, 256, BF16, P, P, N) == MF_EUNSUPPORTED
-    assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 128, BF16, P, P, N) == MF_EUNSUPPORTED
+    assert lib.tp_shard_mlp(P, P, P, P, 4, 160, 256, BF16, P, P, N) == MF_EUNSUPPORTED
+    assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 96, BF16, P, P, N) == MF_EUNSUPPORTED
+    assert lib.tp_shard_mlp(P, P, P, P, 0, 192, 320, BF16, P, P, N) == MF_OK
     assert lib.tp_shard_mlp(P, P, P, P, 4, 256, 256, FP8, P, P, N) == MF_EINVAL
     assert lib.tp_shard_mlp(P, P, P, P, 0, 64, 64, F32, P, P, N) == MF_OK
 
@@ -191,8 +206,9 @@ def test_fp8_prefill_validation(lib):
     assert gu(ri=P, src=0) == MF_EINVAL           # row_index needs src_rows >= 1
     assert gu(xs=N) == MF_EINVAL
     assert gu(ec=257) == MF_EUNSUPPORTED
-    assert gu(d=384) == MF_EUNSUPPORTED           # d % 256
-    assert gu(f=128) == MF_EUNSUPPORTED           # f % 256
+    assert gu(d=320) == MF_EUNSUPPORTED           # d % 128
+    assert gu(f=192) == MF_EUNSUPPORTED           # f % 128
+    assert gu(d=384, f=128, rows=0, xq=N, xs=N, h=N) == MF_OK
     assert gu(d=16640) == MF_EUNSUPPORTED         # contraction above 128 slabs of 128
     assert gu(xq=ctypes.c_void_p(0x100008)) == MF_EUNSUPPORTED
     assert gu(rows=0, xq=N, xs=N, h=N) == MF_OK   # zero rows: nothing to do
@@ -204,7 +220,8 @@ def test_fp8_prefill_validation(lib):
                                    a["wd"], a["sd"], a["y"], N)
     assert dn(sd=N) == MF_EINVAL
     assert dn(y=N) == MF_EINVAL
-    assert dn(f=640) == MF_EUNSUPPORTED
+    assert dn(f=576) == MF_EUNSUPPORTED
+    assert dn(d=128, rows=0, hq=N, hs=N, y=N) == MF_OK
     assert dn(f=16640) == MF_EUNSUPPORTED
     assert dn(rows=0, hq=N, hs=N, y=N) == MF_OK
 
@@ -235,6 +252,6 @@ def test_masked_layout_validation(lib):
     assert gu(cnt=N) == MF_EINVAL
     assert gu(cap=0) == MF_EINVAL
     assert gu(wdt=FP8) == MF_EINVAL        # fp8 weights need their scales
-    assert gu(d=384) == MF_EUNSUPPORTED
+    assert gu(d=352) == MF_EUNSUPPORTED
     assert lib.grouped_down_masked(P, N, 64, 4, 256, 256, P, BF16, N, P, N) == MF_EINVAL
-    assert lib.grouped_down_masked(P, P, 64, 4, 256, 320, P, BF16, N, P, N) == MF_EUNSUPPORTED
+    assert lib.grouped_down_masked(P, P, 64, 4, 256, 288, P, BF16, N, P, N) == MF_EUNSUPPORTED

@@ -94,6 +94,10 @@ def _oracle_w(W, e):
     ([300] * 3 + [0, 77, 513] + [300] * 4, 1024, 512),  # several tiles and rounds
     ([5, 40, 0, 33], 768, 256),   # gate/up: six stages (a four-stage body and a tail)
     ([7, 64], 256, 768),          # down: six stages
+    # odd slab counts (d, f multiples of 128 only) and a down n-tile of 128 rows
+    ([5, 40, 0, 33], 384, 128),   # three and one stages
+    ([7, 64, 200], 640, 640),     # five stages: a four-stage body and one
+    ([3, 300], 896, 1152),        # seven and nine stages
 ])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_a8(g, counts, d, f, gather):

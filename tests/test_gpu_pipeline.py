@@ -192,6 +192,17 @@ def test_moe_ffn_small_fp8_activations(g, T, eb, ec):
     check_layer(g, layer, inp, T, d, f, E, eb, ec, "fp8")
 
 
+@pytest.mark.parametrize("wdtype,d,f,act_fp8", [("bf16", 320, 192, False),
+                                                ("fp8", 384, 640, False),
+                                                ("fp8", 384, 640, True)])
+def test_moe_ffn_sizes_beyond_multiples_of_256(g, wdtype, d, f, act_fp8):
+    # d, f multiples of 64 (bf16) or 128 (fp8) only, end to end
+    T, E, eb, ec = 150, 64, 8, 16
+    inp = make_moe(T, d, f, E, eb, ec, wdtype=wdtype, seed=d + f, device=DEV)
+    layer = build_layer(g, inp, T, d, f, eb, act_fp8=act_fp8)
+    check_layer(g, layer, inp, T, d, f, E, eb, ec, wdtype)
+
+
 def test_moe_ffn_forced_empty_and_single_expert(g):
     # A bias of -10 on every local expert but one: the others get no tokens.
     T, d, f, E, eb, ec = 300, 256, 256, 32, 8, 8

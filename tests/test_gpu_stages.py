@@ -94,7 +94,12 @@ def test_rmsnorm_in_place(g):
                                    (64, 4096, 256), (1000, 1024, 200), (4096, 768, 9),
                                    (129, 2048, 100), (5000, 1024, 256), (2000, 2048, 160),
                                    (600, 768, 256), (256, 4096, 256), (200, 768, 9),
-                                   (33, 1024, 162), (96, 8192, 31)])
+                                   (33, 1024, 162), (96, 8192, 31),
+                                   # hidden sizes that are multiples of 64 only: the
+                                   # few-token kernel, the split-K product with a
+                                   # two-stage K tail, split and unsplit
+                                   (64, 320, 256), (300, 320, 64), (4096, 4224, 256),
+                                   (1000, 4160, 96)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
     idx, w = g.moe_route(r["x"], g.pack_weights(r["w_r"]), r["bias"])
@@ -302,6 +307,24 @@ def test_pack_weights_is_the_documented_permutation(g, fp8, G, N, K):
     assert got.shape == ref.shape and np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("fp8,G,N,K", [(False, 3, 96, 64), (False, 1, 12, 256), (False, 2, 300, 48),
+                                       (True, 2, 48, 256), (True, 1, 20, 128), (True, 3, 200, 384)])
+def test_pack_weights_kn_equals_packing_the_transpose(g, fp8, G, N, K):
+    # a [groups, K, N] source packs to the bytes of its [groups, N, K] transpose
+    dt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    w_kn = synth.normal((G, K, N), name="t.packkn", sub=N, dtype=torch.float32,
+                        device=DEV).to(dt)
+    w_nk = w_kn.transpose(1, 2).contiguous()
+    a = g.pack_weights_kn(w_kn)
+    b = g.pack_weights(w_nk)
+    torch.cuda.synchronize()
+    assert (a.groups, a.N, a.K) == (b.groups, b.N, b.K) == (G, N, K)
+    assert torch.equal(a.data, b.data)
+    view = np.uint8 if fp8 else np.uint16
+    src = w_nk.cpu().view(torch.uint8 if fp8 else torch.int16).numpy().view(view)
+    assert np.array_equal(a.data.cpu().numpy().view(view), _pack_reference(src, fp8).reshape(-1))
+
+
 # ------------------------------------------------------------ grouped GEMM --
 
 def _offsets(counts):
@@ -341,6 +364,15 @@ def _oracle_weights(W, e, wdtype):
     ("fp8", [330] * 4, 1024, 512),
     ("fp8", [200, 45], 8448, 256),    # gate/up contraction of 66 slabs, tiled
     ("fp8", [150], 256, 8448),        # down contraction of 66 slabs, tiled
+    # sizes that are multiples of 64 (bf16) or 128 (fp8) only: K tails of two
+    # stages (bf16) or an odd slab count (fp8), partial last n-tiles
+    ("bf16", [0, 70, 129, 5], 320, 192),
+    ("bf16", [33, 300], 448, 704),
+    ("bf16", [100, 1], 384, 640),
+    ("fp8", [3, 17, 0, 9], 384, 640),        # decode-shaped: 3 and 5 slabs
+    ("fp8", [300, 45, 0, 129], 384, 640),    # tiled: 3 and 5 slabs, down n-tile of 128
+    ("fp8", [3, 9], 8320, 128),              # 65 slabs: a second scale chunk of one slab
+    ("fp8", [200, 45], 8320, 128),           # 65 slabs, tiled
 ])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_swiglu(g, wdtype, counts, d, f, gather):
@@ -468,7 +500,8 @@ def test_tp_shard_f32_dense_config(g):
               rel=1e-5, max_abs=1e-6)
 
 
-@pytest.mark.parametrize("T,d,f,p", [(300, 256, 512, 2), (129, 512, 256, 1), (1, 256, 256, 1)])
+@pytest.mark.parametrize("T,d,f,p", [(300, 256, 512, 2), (129, 512, 256, 1), (1, 256, 256, 1),
+                                     (300, 320, 640, 2), (77, 192, 320, 1)])
 def test_tp_shard_bf16(g, T, d, f, p):
     D = make_dense(T, d, f, dtype=torch.bfloat16, device=DEV, w_std=0.05)
     xf = to_f64(D["x"])
