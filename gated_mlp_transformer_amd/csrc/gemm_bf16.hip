@@ -125,8 +125,16 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f
 //
 // Stage t: (t even) issue the A pair t+2, t+3; issue the weights of t+3; run
 // the MFMAs of t; (t odd) write the A pair loaded at stage t-1 into its two
-// LDS buffers; barrier. Thread (ld_r, ld_c) moves 16-byte chunk ld_c of the
-// 128-byte pair segment of rows ld_r + 32i, i < NM.
+// LDS buffers, then barrier. Thread (ld_r, ld_c) moves 16-byte chunk ld_c of
+// the 128-byte pair segment of rows ld_r + 32i, i < NM.
+//
+// One barrier per stage pair is enough. The pair written at odd stage t goes
+// to buffers (t+1)%4 and (t+2)%4. Any wave that has not reached this write is
+// at stage t-1 or t, reading buffer (t-1)%4 or t%4, which are different
+// buffers. The barrier at the end of stage t-2 ordered the last reads of the
+// two target buffers (stages t-3 and t-2) before the write. The barrier at
+// the end of stage t makes the written pair visible to stages t+1 and t+2.
+// Measured 1 % faster at prefill than a barrier after every stage.
 template <int MT, int NM, bool TAIL>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
                                        const int (&arow)[MT], int64_t Kb,
@@ -232,7 +240,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
     const int t_ = kt + (S);                                                               \
     stage(breg[(S)], (S), ((S) & 1) == 0, min(t_ + 2, nk - 2), breg[((S) + PREF) % SLOTS],  \
           min(t_ + PREF, nk - 1));                                                         \
-    __syncthreads();                                                                       \
+    if ((S) & 1) __syncthreads();                                                          \
   }
   int kt = 0;
   for (; TAIL ? kt + SLOTS <= nk : kt < nk; kt += SLOTS) {
