@@ -171,6 +171,53 @@ def warm_clock(seconds=0.25):
         torch.cuda.synchronize()
 
 
+def process_warmup(iters=60):
+    """Untimed, once per process before the first timed workload: small
+    instances of every pipeline the bench times (1024-token prefill layers
+    with 4 local experts in bf16, fp8-activation and fp8-weight form, 64-token
+    decode layers with 16 local experts in both layouts, a 512-token dense
+    shard and the fp32 dense shard), `iters` forwards each, through the same
+    kernels. The first layer a process runs was otherwise slow for tens of
+    steps whatever the clock: 1658, 822, 771, 760 µs per step over its first
+    four 5-step windows against ≈ 755 µs after, while a fresh full-size layer
+    built after this warm-up started at 762 µs. Each timed workload still
+    gets exactly W warm-up steps of its own. Returns a description."""
+    import torch
+    import gated_mlp_transformer_amd as g
+    import synth
+    from synth.workloads import make_dense, shard_weights
+    W = synth.WORKLOADS
+    small = [dict(W[PREFILL], T=1024, e_count=4), dict(W[PREFILL_FP8], T=1024, e_count=4),
+             dict(W[PREFILL_FP8W], T=1024, e_count=4), dict(W[DECODE], e_count=16),
+             dict(W[DECODE_MASKED], e_count=16)]
+    for spec in small:
+        for norm in ((True, False) if spec is small[0] else (True,)):
+            layer, inp = build_layer(spec, "cuda", seed=7, norm=norm)
+            for _ in range(iters):
+                layer(inp["x"])
+            torch.cuda.synchronize()
+            del layer, inp
+    D = make_dense(512, 4096, 2048, dtype=torch.bfloat16, norm=True, device="cuda", seed=7)
+    packed = [g.pack_weights(D[k]) for k in ("w_gate", "w_up", "w_down")]
+    v = torch.empty_like(D["x"])
+    for _ in range(iters):
+        g.rmsnorm(D["x"], D["gamma"], 1e-5, out=v)
+        g.tp_shard_mlp(v, *packed)
+    spec32 = W["dense_f32_16x64_f256_p4"]
+    D32 = make_dense(spec32["T"], spec32["d"], spec32["f"], dtype=torch.float32, device="cuda")
+    sh = shard_weights(D32["w_gate"], D32["w_up"], D32["w_down"], spec32["p"], 0)
+    for _ in range(iters):
+        g.tp_shard_mlp(D32["x"], *sh)
+    torch.cuda.synchronize()
+    del D, packed, v, D32, sh
+    torch.cuda.empty_cache()
+    return (f"untimed, before the first timed workload: {iters} forwards each of small "
+            "instances of every timed pipeline (1024-token prefill layers with 4 local experts "
+            "in bf16 with and without RMSNorm, fp8-activation and fp8-weight form; 64-token "
+            "decode layers with 16 local experts, contiguous and masked; a 512-token dense "
+            "shard; the fp32 dense shard), through the same kernels")
+
+
 def time_layer(layer, x, steps, warmup):
     """Warm up, then time exactly `steps` forwards back to back between two
     events. The per-stage breakdown comes from a second pass of `steps`
@@ -706,6 +753,8 @@ def main():
     attain = measure_attainable()
     log(f"[bench] attainable: {attain['mfma_bf16_tflop_s']} TFLOP/s bf16 MFMA, "
         f"{attain['hbm_gb_s']} GB/s HBM read, {attain['hbm_rw_gb_s']} GB/s read + write")
+    warm_desc = process_warmup()
+    log("[bench] process warm-up done")
     # written before every flushed rep: larger than the 256 MB last-level cache
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
 
@@ -729,7 +778,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(res["ms"], 4),
-        # per-step times of the same timed steps (first stage mark to last)
+        # before the first workload's own W warm-up steps (untimed)
+        "process_warmup": warm_desc,
+        # per-step times of K more steps with an event between stages (first
+        # stage mark to last)
         "step_us_median": round(step["median"], 2),
         "step_us_min": round(step["min"], 2),
         # K further steps, each after an untimed 512 MB scratch write
