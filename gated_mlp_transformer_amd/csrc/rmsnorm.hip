@@ -160,8 +160,9 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
                                                            float* __restrict__ qs) {
   const int lane = threadIdx.x % kWave;
   const char* gr = reinterpret_cast<const char*>(gamma) + lane * 16;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; row < rows;
+  const int wpg = blockDim.x / kWave;  // one row per wave: 4 per workgroup, or 1 for few rows
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * wpg;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * wpg + threadIdx.x / kWave; row < rows;
        row += stride) {
     const char* xr = reinterpret_cast<const char*>(x + row * d) + lane * 16;
     u32x4 v[NV], gv[NV];
@@ -238,11 +239,15 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
   auto* gp = static_cast<const T*>(gamma);
   auto* yp = static_cast<T*>(y);
   if (rows <= 1024) {  // few rows: gamma with the row (one round trip)
+    // up to 256 rows: one row per 64-thread workgroup, spread over as many CUs
+    const bool spread = rows <= 256;
+    const dim3 g1 = spread ? dim3(static_cast<unsigned>(rows < 1 ? 1 : rows)) : grid;
+    const int nt = spread ? kWave : 256;
     switch (per_lane) {
-      case 1: rmsnorm_full_kernel<T, 1, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 2: rmsnorm_full_kernel<T, 2, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 4: rmsnorm_full_kernel<T, 4, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 8: rmsnorm_full_kernel<T, 8, true><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 1: rmsnorm_full_kernel<T, 1, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 2: rmsnorm_full_kernel<T, 2, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 4: rmsnorm_full_kernel<T, 4, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 8: rmsnorm_full_kernel<T, 8, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
       default: break;  // wider rows: the kernels below
     }
   }

@@ -226,7 +226,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
   __shared__ float s_sc[4][8];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  // one token per wave: four per workgroup, or one for few tokens
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + wave;
   if (t >= T) return;
   const int64_t split_stride = T * E;
   // candidates of this lane: experts 4 lane + c
@@ -279,13 +280,17 @@ void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, 
   } else {
     launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
   }
-  const dim3 grid(static_cast<unsigned>((T + 3) / 4));
+  // few tokens: one token per 64-thread workgroup, so that the partial
+  // logits are read by as many CUs as there are tokens
+  const bool spread = T <= kSmallT;
+  const dim3 grid(static_cast<unsigned>(spread ? T : (T + 3) / 4));
+  const int nt = spread ? kWave : 256;
   switch (splits) {  // route_splits returns a power of two <= kMaxSplits
-    case 1: route_select_kernel<1><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
-    case 2: route_select_kernel<2><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
-    case 4: route_select_kernel<4><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
-    case 8: route_select_kernel<8><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
-    default: route_select_kernel<kMaxSplits><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 1: route_select_kernel<1><<<grid, nt, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 2: route_select_kernel<2><<<grid, nt, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 4: route_select_kernel<4><<<grid, nt, 0, s>>>(zp, bias, T, E, idx, w); break;
+    case 8: route_select_kernel<8><<<grid, nt, 0, s>>>(zp, bias, T, E, idx, w); break;
+    default: route_select_kernel<kMaxSplits><<<grid, nt, 0, s>>>(zp, bias, T, E, idx, w); break;
   }
 }
 
