@@ -324,9 +324,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   const int64_t kofs_b = static_cast<int64_t>(blockIdx.y) * (p.kc / 16) * FRAG;
   char* const cbase = p.c + static_cast<int64_t>(blockIdx.y) * p.c_split * (OUT_F32 ? 4 : 2);
 
+  // Split tail. The tiles past the last full round of G would leave the other
+  // workgroups idle for a whole tile time (prefill gate/up: 896 tiles on 256
+  // workgroups, busy 277-413 us against a 413 us launch). When that round is
+  // at most half full, each of its tiles runs as two units, each with half of
+  // the chunk's sub-tiles over the whole contraction: no partial sums to
+  // exchange, every output row written by one workgroup, the same arithmetic.
+  const int full_t = (total_tiles / G) * G;
+  const int tail_t = total_tiles - full_t;
+  const bool split = MT == 8 && tail_t > 0 && 2 * tail_t <= G;
+  const int total_units = split ? full_t + 2 * tail_t : total_tiles;
+
   for (int it = 0;; it += G) {
-    const int L = it + xcd * (G >> 3) + slot;
-    if (L >= total_tiles) break;
+    const int U = it + xcd * (G >> 3) + slot;
+    if (U >= total_units) break;
+    // tile L; for a split tail tile, its first (half 0) or second row half
+    int L = U, half = -1;
+    if (split && U >= full_t) {
+      L = full_t + ((U - full_t) >> 1);
+      half = (U - full_t) & 1;
+    }
 
     // group e: the last with s_tile0[e] <= L (it owns tile L)
     int lo = 0, hi = p.e_count - 1;
@@ -340,8 +357,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     const int nch = (sub_e + Z - 1) / Z;
     const int ni = t / nch, mi = t - ni * nch;  // n-tile major, chunk minor
     const int q = sub_e / nch, r = sub_e - q * nch;
-    const int z0 = mi * q + min(mi, r);            // first sub-tile of the chunk
-    const int nm = q + (mi < r ? 1 : 0);           // sub-tiles in the chunk
+    const int zc = mi * q + min(mi, r);            // first sub-tile of the chunk
+    const int nmc = q + (mi < r ? 1 : 0);          // sub-tiles in the chunk
+    // a split tail tile: the first ceil(nmc/2) sub-tiles, or the rest
+    const int z0 = half > 0 ? zc + (nmc + 1) / 2 : zc;
+    const int nm = half < 0 ? nmc : (half == 0 ? (nmc + 1) / 2 : nmc / 2);
+    if (nm == 0) continue;  // the second half of a one-sub-tile chunk
     const int row0 = s_beg[e] + z0 * 32;
     const int rows_valid = min(nm * 32, s_end[e] - row0);
     const int n0 = ni * BN_OUT;

@@ -355,6 +355,11 @@ def _oracle_weights(W, e, wdtype):
     ("bf16", [0, 0, 0], 256, 256),
     ("bf16", [1, 33, 65, 97, 128, 129, 31, 32], 256, 256),   # every tail sub-tile count
     ("bf16", [300] * 5 + [0, 77, 513] + [300] * 8, 1024, 1024),  # > 256 tiles: several rounds
+    # a last round at most half full runs its tiles as two row halves (with
+    # 256 CUs, gate/up here: 264 tiles = one full round + 8 split; the case
+    # above with every tail sub-tile count splits its down GEMM, one-sub-tile
+    # chunks included, whose second half is empty)
+    ("bf16", [300] * 66, 256, 256),
     ("fp8", [1, 3, 0, 17, 2, 16], 256, 512),
     ("fp8", [40], 512, 256),
     ("bf16", [(7 * e) % 5 for e in range(256)], 256, 256),   # the most groups (256)
