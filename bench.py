@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first copy a 1 GiB device buffer 3 times (a kernel of "
                          "known traffic to scale HBM byte counters against)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="with --only: skip the HIP-graph replays, so that a kernel trace "
+                         "averages the eagerly launched steps the line reports")
     return ap.parse_args()
 
 
@@ -732,7 +735,7 @@ def main():
         if args.only in ("prefill", "decode", "prefill_fp8", "decode_masked", "prefill_fp8w"):
             name = {"prefill": PREFILL, "decode": DECODE, "prefill_fp8": PREFILL_FP8,
                     "decode_masked": DECODE_MASKED, "prefill_fp8w": PREFILL_FP8W}[args.only]
-            res = run_moe(name, args.steps, args.warmup)
+            res = run_moe(name, args.steps, args.warmup, graph=not args.no_graph)
             peak = PEAK_FP8_TFLOPS if res["spec"].get("act_fp8") else PEAK_BF16_TFLOPS
             print(json.dumps(dict(workload=res["spec"], ms_per_step=res["ms"],
                                   graph_ms_per_step=res["ms_graph"],
