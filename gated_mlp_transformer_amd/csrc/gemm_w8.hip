@@ -227,9 +227,23 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
   const int nk = KB;
   const int64_t Kb = static_cast<int64_t>(p.K) * 2;  // bytes per A row
 
+  // Split tail (as in the bf16 grouped GEMM): a last round of tiles that is
+  // at most half full runs each of its tiles as two units with half of the
+  // tile's sub-tiles each, over the whole contraction.
+  const int full_t = (total_tiles / G) * G;
+  const int tail_t = total_tiles - full_t;
+  const bool split = tail_t > 0 && 2 * tail_t <= G;
+  const int total_units = split ? full_t + 2 * tail_t : total_tiles;
+
   for (int it = 0;; it += G) {
-    const int L = it + xcd * (G >> 3) + slot;
-    if (L >= total_tiles) break;
+    const int U = it + xcd * (G >> 3) + slot;
+    if (U >= total_units) break;
+    // tile L; for a split tail tile, its first (half 0) or second row half
+    int L = U, half = -1;
+    if (split && U >= full_t) {
+      L = full_t + ((U - full_t) >> 1);
+      half = (U - full_t) & 1;
+    }
     int lo = 0, hi = p.e_count - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -241,8 +255,12 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
     const int nch = (sub_e + MT - 1) / MT;
     const int ni = t / nch, mi = t - ni * nch;  // n-tile major, chunk minor
     const int q = sub_e / nch, r = sub_e - q * nch;
-    const int z0 = mi * q + min(mi, r);
-    const int nm = q + (mi < r ? 1 : 0);
+    const int zc = mi * q + min(mi, r);   // first sub-tile of the chunk
+    const int nmc = q + (mi < r ? 1 : 0); // sub-tiles in the chunk
+    // a split tail tile: the first ceil(nmc/2) sub-tiles, or the rest
+    const int z0 = half > 0 ? zc + (nmc + 1) / 2 : zc;
+    const int nm = half < 0 ? nmc : (half == 0 ? (nmc + 1) / 2 : nmc / 2);
+    if (nm == 0) continue;  // the second half of a one-sub-tile chunk
     const int row0 = s_beg[e] + z0 * 32;
     const int rows_valid = min(nm * 32, s_end[e] - row0);
     const int n0 = ni * BN_OUT;
