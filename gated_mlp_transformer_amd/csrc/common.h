@@ -109,6 +109,13 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// 16 bytes of data that is read once (weights streamed through a kernel):
+// a non-temporal load. On this chip 16-byte streaming reads of a 4 GiB buffer
+// reach 7.1-7.3 TB/s with the non-temporal policy against 6.0-6.2 TB/s with
+// the default one (one to four workgroups per CU, 8 or 16 loads in flight).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Buffer resource over [p, p + 2^31) for raw buffer loads: p must be the same
 // for every lane of the wave (it is read from the first lane), offsets are

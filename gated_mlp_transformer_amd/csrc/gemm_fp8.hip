@@ -163,9 +163,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
         const int64_t kofs = static_cast<int64_t>(kb) * SLAB;
         const int64_t bofs = static_cast<int64_t>(kb) * slab_stride;
 #pragma unroll
-        for (int q = 0; q < R; ++q) {
-          s.b[q][0] = ld16(wp[q] + bofs);
-          s.b[q][1] = ld16(wp[q] + bofs + 1024);
+        for (int q = 0; q < R; ++q) {  // each weight byte is read once: streamed
+          s.b[q][0] = ld16_stream(wp[q] + bofs);
+          s.b[q][1] = ld16_stream(wp[q] + bofs + 1024);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) s.a[c] = ld16(ap + kofs * 2 + 16 * c);
