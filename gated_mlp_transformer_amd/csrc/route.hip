@@ -72,6 +72,15 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
+// sigmoid(z) = 1 / (1 + 2^(-z log2(e))) on the hardware exp2 and reciprocal
+// (each within about 1 ulp): about 3e-7 absolute error in s, against the 1e-6
+// margin within which two biased scores count as a near tie. An IEEE divide
+// and a range-reduced expf cost about 18 instructions per score here, and the
+// selection runs 256 of them per token.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504f));
+}
+
 }  // namespace
 
 // Token counts up to this take the few-token logits kernel.
@@ -261,10 +270,145 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
     float z = 0.f;
 #pragma unroll
     for (int y = 0; y < SPLITS; ++y) z += part[y][c];
-    sc[c] = sigmoidf_(z);
+    sc[c] = sigmoid_hw(z);
     key[c] = e < E ? order_key(sc[c] + bias[min(e, E - 1)]) : 0u;
   }
   select_top8(key, sc, lane, idx_out + t * 8, w_out + t * 8, s_sc[wave]);
+}
+
+// Many tokens: four tokens per wavefront, one 16-lane DPP row each (a round's
+// maxima stay inside the row: four DPP steps, every lane of the row holds the
+// result, no lane read). Lane j of a row holds experts 64q + 4j + c
+// (q, c = 0..3), so each split's partials of a token arrive as four 16-byte
+// loads per lane, each load instruction covering 256 contiguous bytes of the
+// row. A wave per token (the kernel above) spends most of its instructions on
+// wave-wide reductions whose steps do one useful compare per lane; here a
+// round costs about 90 instructions for four tokens. Same arithmetic and
+// order as route_select_kernel: the partials summed in split order, then
+// sigmoid, bias, the order-preserving key, ties to the lower id, the eight
+// scores summed in ascending id order.
+__device__ __forceinline__ uint32_t row_umax(uint32_t v) {
+  v = max(v, dpp_or0<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_or0<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_or0<0x141, 0xF>(v));  // row_half_mirror: the 8-lane half
+  v = max(v, dpp_or0<0x140, 0xF>(v));  // row_mirror: the 16-lane row
+  return v;
+}
+
+__device__ __forceinline__ void cex(int& a, int& b) {
+  const int lo = min(a, b), hi = max(a, b);
+  a = lo;
+  b = hi;
+}
+
+template <int SPLITS>
+__global__ __launch_bounds__(256) void route_select_rows_kernel(const float* __restrict__ zp,
+                                                                const float* __restrict__ bias,
+                                                                int64_t T, int E,
+                                                                int32_t* __restrict__ idx_out,
+                                                                float* __restrict__ w_out) {
+  __shared__ float s_bias[256];
+  __shared__ float s_sc[16][256];  // the scores of the workgroup's 16 tokens
+  const int lane = threadIdx.x % kWave;
+  const int slot = threadIdx.x / 16;  // token of the workgroup: wave * 4 + row
+  const int j = lane & 15;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16 + slot;
+  const int64_t t = min(t0, T - 1);  // rows past T redo token T-1 and store nothing
+  s_bias[threadIdx.x] = bias[min(static_cast<int>(threadIdx.x), E - 1)];
+  __syncthreads();
+  const int64_t split_stride = T * E;
+  // z summed in split order; the loads of up to eight splits are in flight
+  // together (all of them for the split counts the prefill sizes use)
+  constexpr int CH = SPLITS < 8 ? SPLITS : 8;
+  float z[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+#pragma unroll
+  for (int y0 = 0; y0 < SPLITS; y0 += CH) {
+    float part[CH][16];
+    if ((E & 3) == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int ev = min(64 * q + 4 * j, E - 4);  // lanes past E re-read the last four
+#pragma unroll
+        for (int y = 0; y < CH; ++y) {
+          const u32x4 v = ld16(zp + (y0 + y) * split_stride + t * E + ev);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) part[y][4 * q + c] = __uint_as_float(v[c]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int y = 0; y < CH; ++y)
+            part[y][4 * q + c] =
+                zp[(y0 + y) * split_stride + t * E + min(64 * q + 4 * j + c, E - 1)];
+    }
+#pragma unroll
+    for (int y = 0; y < CH; ++y)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] += part[y][i];
+  }
+  float* srow = s_sc[slot];
+  uint32_t key[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int eb = 64 * q + 4 * j;
+    const f32x4 b4 = *reinterpret_cast<const f32x4*>(s_bias + eb);
+    f32x4 s4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      s4[c] = sigmoid_hw(z[4 * q + c]);
+      key[4 * q + c] = eb + c < E ? order_key(s4[c] + b4[c]) : 0u;
+    }
+    *reinterpret_cast<f32x4*>(srow + eb) = s4;
+  }
+  // Eight rounds: the row's maximum key m; the lowest expert id holding it
+  // (each lane's lowest slot holding m, slots being in id order within a
+  // lane, then the row maximum of 256 - id); the owner lane retires it.
+  int win[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) lm = max(lm, key[i]);
+    const uint32_t m = row_umax(lm);
+    int lo = 16;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) lo = key[i] == m ? i : lo;
+    const uint32_t cand =
+        lo < 16 ? 256u - static_cast<uint32_t>(64 * (lo >> 2) + 4 * j + (lo & 3)) : 0u;
+    const int e = 256 - static_cast<int>(row_umax(cand));
+    win[r] = e;
+    // the winner's slot in its owner lane; 16 or more in every other lane
+    const int own = (4 * (e >> 6) + (e & 3)) | ((((e >> 2) & 15) ^ j) << 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) key[i] = own == i ? 0u : key[i];
+  }
+  // ids ascending (a 19-comparator network on the row-uniform winners)
+  cex(win[0], win[2]); cex(win[1], win[3]); cex(win[4], win[6]); cex(win[5], win[7]);
+  cex(win[0], win[4]); cex(win[1], win[5]); cex(win[2], win[6]); cex(win[3], win[7]);
+  cex(win[0], win[1]); cex(win[2], win[3]); cex(win[4], win[5]); cex(win[6], win[7]);
+  cex(win[2], win[4]); cex(win[3], win[5]);
+  cex(win[1], win[4]); cex(win[3], win[6]);
+  cex(win[1], win[2]); cex(win[3], win[4]); cex(win[5], win[6]);
+  // the scores were written by other lanes of this wavefront
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float sum = 0.f;  // in ascending id order
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += srow[win[i]];
+  int mine = win[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mine = j == i ? win[i] : mine;
+  if (j < 8 && t0 < T) {
+    idx_out[t0 * 8 + j] = mine;
+    w_out[t0 * 8 + j] = srow[mine] / sum;
+  }
 }
 
 void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, int d, int E,
@@ -279,6 +423,19 @@ void launch_route(const void* x, const void* w_r, const float* bias, int64_t T, 
                                                 d, E, d / splits, zp);
   } else {
     launch_gemm_nt_f32_splitk(x, T, d, w_r, E, splits, zp, num_cus, s);
+  }
+  if (T > kSmallT) {  // sixteen tokens per 256-thread workgroup
+    const dim3 grid(static_cast<unsigned>((T + 15) / 16));
+    switch (splits) {  // route_splits returns a power of two <= kMaxSplits
+      case 1: route_select_rows_kernel<1><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+      case 2: route_select_rows_kernel<2><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+      case 4: route_select_rows_kernel<4><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+      case 8: route_select_rows_kernel<8><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w); break;
+      default:
+        route_select_rows_kernel<kMaxSplits><<<grid, 256, 0, s>>>(zp, bias, T, E, idx, w);
+        break;
+    }
+    return;
   }
   // few tokens: one token per 64-thread workgroup, so that the partial
   // logits are read by as many CUs as there are tokens

@@ -114,12 +114,14 @@ def test_route(g, T, d, E):
     assert np.allclose(to_f64(w).sum(1), 1.0, atol=1e-5)
 
 
-def test_route_exact_ties_pick_lower_index(g):
-    # Only 4 distinct router rows, each repeated 16 times, and a zero bias:
+@pytest.mark.parametrize("T,E", [(200, 64), (600, 64), (1000, 256)])
+def test_route_exact_ties_pick_lower_index(g, T, E):
+    # Only E/16 distinct router rows, each repeated 16 times, and a zero bias:
     # every token has exact ties inside its winning group, and the 8 lowest
-    # ids of the group with the highest score must be chosen.
-    T, d, E = 200, 256, 64
-    base = synth.normal((4, d), name="t.tie.w", std=0.05, device=DEV)
+    # ids of the group with the highest score must be chosen. T = 200 takes
+    # the few-token kernels, the larger T the many-token selection.
+    d = 256
+    base = synth.normal((E // 16, d), name="t.tie.w", std=0.05, device=DEV)
     w_r = base.repeat_interleave(16, dim=0).contiguous()
     x = synth.normal((T, d), name="t.tie.x", device=DEV)
     bias = torch.zeros(E, dtype=torch.float32, device=DEV)
