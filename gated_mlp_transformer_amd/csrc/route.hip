@@ -16,20 +16,26 @@
 //       permuted contraction order, the matching 16-byte slots of the packed
 //       weight fragments; every load of the K range is in flight before the
 //       first MFMA.
-//  2. select: one wavefront per token sums the partials in split order (fixed
-//     order: deterministic), applies the sigmoid and the bias, and picks the
-//     top 8 by eight rounds of a wave-wide arg-max on (key descending, id
-//     ascending); the ids are emitted ascending with w = s / sum(s).
-//     Lane l holds experts 4l .. 4l+3, so each split's partials of a token
-//     arrive with one 16-byte load per lane (1 KB per wave instruction).
-//     A round takes the wave-wide maximum of the keys (mapped to
-//     order-preserving unsigned integers) with DPP max steps at register
-//     speed, then the lowest expert id that holds it as a second DPP
-//     maximum (of 256 - id over the lanes' candidates equal to the key
-//     maximum). Only that candidate is retired, so equal keys are taken in
-//     ascending id order over the rounds. A winner's output slot is its rank
-//     among the winners by id (popcounts of per-slot ballots), and the eight
-//     scores are summed in that order.
+//  2. select: sums each token's partials in split order (fixed order:
+//     deterministic), applies the sigmoid and the bias, and picks the top 8
+//     by eight rounds of an arg-max on (key descending, id ascending); the
+//     ids are emitted ascending with w = s / sum(s).
+//     - Few tokens: one wavefront per token. Lane l holds experts 4l .. 4l+3,
+//       so each split's partials of a token arrive with one 16-byte load per
+//       lane (1 KB per wave instruction). A round takes the wave-wide maximum
+//       of the keys (mapped to order-preserving unsigned integers) with DPP
+//       max steps, then the lowest expert id that holds it as a second DPP
+//       maximum (of 256 - id over the lanes' candidates equal to the key
+//       maximum). Only that candidate is retired, so equal keys are taken in
+//       ascending id order over the rounds. A winner's output slot is its
+//       rank among the winners by id (popcounts of per-slot ballots), and the
+//       eight scores are summed in that order.
+//     - Many tokens: the same rounds with one 16-lane DPP row per token, four
+//       tokens per wavefront (route_select_rows_kernel). The selection is
+//       bound by its vector instructions, not by its loads: a wave per token
+//       issued about 600 of them per token, mostly wave-wide reduction steps
+//       that do one useful compare per lane; a row per token issues about
+//       260.
 #include "common.h"
 #include "launch.h"
 
