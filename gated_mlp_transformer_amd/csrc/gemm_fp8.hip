@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(Fp8Params p) {
   s_item0[tid + 1] = items;  // inclusive scan below, shifted by one
   if (tid == 0) s_item0[0] = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
+  for (int off = 1; off < p.e_count; off <<= 1) {  // entries 0 .. e_count are read
     const int v = tid >= off ? s_item0[tid + 1 - off] : 0;
     __syncthreads();
     s_item0[tid + 1] += v;

@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w8_kernel(W8Params p) {
   s_tile0[tid + 1] = ntile;
   if (tid == 0) s_tile0[0] = 0;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
+  for (int off = 1; off < p.e_count; off <<= 1) {  // entries 0 .. e_count are read
     const int v = tid >= off ? s_tile0[tid + 1 - off] : 0;
     __syncthreads();
     s_tile0[tid + 1] += v;
