@@ -153,7 +153,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 // row's, so that they are not a second round trip after the sum; for many
 // rows they come after it, which keeps the kernel at fewer registers (more
 // waves per SIMD, more row loads in flight).
-template <typename T, int NV, bool GPRE>
+// QUANT (bf16 only) adds the fp8 codes of the output; it is a separate
+// instantiation because the encode path's registers would otherwise cost the
+// plain kernel waves per SIMD (102 against 69 VGPRs at d = 4096).
+template <typename T, int NV, bool GPRE, bool QUANT>
 __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
                                                            T* y, int64_t rows, int d, float eps,
                                                            uint8_t* __restrict__ q,
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
 #pragma unroll
         for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
         o = pack_bf16x8(res);
-        if (q != nullptr) {
+        if constexpr (QUANT) {
           const int vi = lane + i * kWave;
           quant_group_store(o, lane, q + row * d + static_cast<int64_t>(vi) * 8,
                             qs + row * (d / 128) + vi / 16);
@@ -227,9 +230,9 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
 
 namespace {
 
-template <typename T>
-bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d, float eps,
-                 uint8_t* q, float* qs, hipStream_t s) {
+template <typename T, bool QUANT>
+bool launch_full_q(const void* x, const void* gamma, void* y, int64_t rows, int d, float eps,
+                   uint8_t* q, float* qs, hipStream_t s) {
   const int per_lane = d * static_cast<int>(sizeof(T)) / (16 * kWave);  // vectors per lane
   if (d * static_cast<int>(sizeof(T)) % (16 * kWave) != 0) return false;
   int64_t blocks = (rows + 3) / 4;
@@ -244,27 +247,36 @@ bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d,
     const dim3 g1 = spread ? dim3(static_cast<unsigned>(rows < 1 ? 1 : rows)) : grid;
     const int nt = spread ? kWave : 256;
     switch (per_lane) {
-      case 1: rmsnorm_full_kernel<T, 1, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 2: rmsnorm_full_kernel<T, 2, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 4: rmsnorm_full_kernel<T, 4, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-      case 8: rmsnorm_full_kernel<T, 8, true><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 1: rmsnorm_full_kernel<T, 1, true, QUANT><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 2: rmsnorm_full_kernel<T, 2, true, QUANT><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 4: rmsnorm_full_kernel<T, 4, true, QUANT><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+      case 8: rmsnorm_full_kernel<T, 8, true, QUANT><<<g1, nt, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
       default: break;  // wider rows: the kernels below
     }
   }
   switch (per_lane) {
-    case 1: rmsnorm_full_kernel<T, 1, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 2: rmsnorm_full_kernel<T, 2, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 4: rmsnorm_full_kernel<T, 4, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 8: rmsnorm_full_kernel<T, 8, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
-    case 16: rmsnorm_full_kernel<T, 16, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 1: rmsnorm_full_kernel<T, 1, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 2: rmsnorm_full_kernel<T, 2, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 4: rmsnorm_full_kernel<T, 4, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 8: rmsnorm_full_kernel<T, 8, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
+    case 16: rmsnorm_full_kernel<T, 16, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs); return true;
     case 32:  // f32 rows of 8192
       if constexpr (sizeof(T) == 4) {
-        rmsnorm_full_kernel<T, 32, false><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs);
+        rmsnorm_full_kernel<T, 32, false, QUANT><<<grid, 256, 0, s>>>(xp, gp, yp, rows, d, eps, q, qs);
         return true;
       }
       return false;
     default: return false;
   }
+}
+
+template <typename T>
+bool launch_full(const void* x, const void* gamma, void* y, int64_t rows, int d, float eps,
+                 uint8_t* q, float* qs, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (q != nullptr) return launch_full_q<T, true>(x, gamma, y, rows, d, eps, q, qs, s);
+  }
+  return launch_full_q<T, false>(x, gamma, y, rows, d, eps, nullptr, nullptr, s);
 }
 
 }  // namespace
