@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 // waves per SIMD, more row loads in flight).
 // QUANT (bf16 only) adds the fp8 codes of the output; it is a separate
 // instantiation because the encode path's registers would otherwise cost the
-// plain kernel waves per SIMD (102 against 69 VGPRs at d = 4096).
+// plain kernel waves per SIMD (102 against 61 VGPRs at d = 4096).
 template <typename T, int NV, bool GPRE, bool QUANT>
 __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
                                                            T* y, int64_t rows, int d, float eps,
@@ -207,12 +207,14 @@ __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* 
       const u32x4 g = GPRE ? gv[i] : ld16(gr + i * kWave * 16);
       u32x4 o;
       if constexpr (sizeof(T) == 2) {
-        float f[8], gf[8], res[8];
-        unpack_bf16x8(v[i], f);
-        unpack_bf16x8(g, gf);
+        // pair by pair (no unpacked copy of the slice): 61 VGPRs at d = 4096,
+        // eight waves per SIMD, every row of the 8192-row prefill resident at
+        // once (with the slice unpacked, 67 VGPRs left a second round of 1024)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) res[e] = gf[e] * (f[e] * r);
-        o = pack_bf16x8(res);
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(__uint_as_float(g[e] << 16) * (__uint_as_float(v[i][e] << 16) * r),
+                             __uint_as_float(g[e] & 0xFFFF0000u) *
+                                 (__uint_as_float(v[i][e] & 0xFFFF0000u) * r));
         if constexpr (QUANT) {
           const int vi = lane + i * kWave;
           quant_group_store(o, lane, q + row * d + static_cast<int64_t>(vi) * 8,
