@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* x, const T* __res
 // waves per SIMD, more row loads in flight).
 // QUANT (bf16 only) adds the fp8 codes of the output; it is a separate
 // instantiation because the encode path's registers would otherwise cost the
-// plain kernel waves per SIMD (102 against 61 VGPRs at d = 4096).
+// plain kernel waves per SIMD (101 against 61 VGPRs at d = 4096).
 template <typename T, int NV, bool GPRE, bool QUANT>
 __global__ __launch_bounds__(256) void rmsnorm_full_kernel(const T* x, const T* __restrict__ gamma,
                                                            T* y, int64_t rows, int d, float eps,
