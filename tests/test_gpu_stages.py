@@ -101,7 +101,11 @@ def test_rmsnorm_in_place(g):
                                    # few-token kernel, the split-K product with a
                                    # two-stage K tail, split and unsplit
                                    (64, 320, 256), (300, 320, 64), (4096, 4224, 256),
-                                   (1000, 4160, 96)])
+                                   (1000, 4160, 96),
+                                   # many-token selection at prefill sizes (two
+                                   # or four splits, a ragged last workgroup),
+                                   # and a large T with E not a multiple of 4
+                                   (8200, 1024, 256), (8192, 2048, 64), (9000, 512, 9)])
 def test_route(g, T, d, E):
     r = make_router(T, d, E, seed=T + d + E, device=DEV)
     idx, w = g.moe_route(r["x"], g.pack_weights(r["w_r"]), r["bias"])
@@ -114,7 +118,7 @@ def test_route(g, T, d, E):
     assert np.allclose(to_f64(w).sum(1), 1.0, atol=1e-5)
 
 
-@pytest.mark.parametrize("T,E", [(200, 64), (600, 64), (1000, 256)])
+@pytest.mark.parametrize("T,E", [(200, 64), (600, 64), (1000, 256), (8200, 256)])
 def test_route_exact_ties_pick_lower_index(g, T, E):
     # Only E/16 distinct router rows, each repeated 16 times, and a zero bias:
     # every token has exact ties inside its winning group, and the 8 lowest
