@@ -31,11 +31,10 @@
 //       rank among the winners by id (popcounts of per-slot ballots), and the
 //       eight scores are summed in that order.
 //     - Many tokens: the same rounds with one 16-lane DPP row per token, four
-//       tokens per wavefront (route_select_rows_kernel). The selection is
-//       bound by its vector instructions, not by its loads: a wave per token
-//       issued about 600 of them per token, mostly wave-wide reduction steps
-//       that do one useful compare per lane; a row per token issues about
-//       260.
+//       tokens per wavefront (route_select_rows_kernel). At these sizes a
+//       wave per token was bound by its vector instructions, not by its
+//       loads: about 600 per token, mostly wave-wide reduction steps that do
+//       one useful compare per lane; a row per token issues about 260.
 #include "common.h"
 #include "launch.h"
 
