@@ -13,11 +13,16 @@
 // rows against 256 weight rows: 128 gate + 128 up rows (128 output columns,
 // gate and up side by side so the SiLU product stays in registers) or 256 down
 // rows (256 output columns). Each wave owns 64 weight rows (two 32-row
-// fragments) for all the tile's rows: 2*MT 32x32 accumulators, kept in AGPRs
-// and accumulated in place. The grouped GEMMs use MT = 8 (256 rows, the whole
-// AGPR file): per 32-deep K stage a workgroup moves 32 KB (A 16 KB + weights
-// 16 KB) for 1024 MFMA cycles per SIMD, two thirds of the bytes per flop of
-// 128-row tiles. The router's split-K product uses MT = 4.
+// fragments) for all the tile's rows: 2*MT 32x32 accumulators, accumulated in
+// place. The grouped GEMMs and the dense TP shard use MT = 4 (128 rows) with
+// two workgroups per CU (OCC = 2: 256 registers per wave, two waves per SIMD),
+// so that one wave's MFMAs issue while the other waits on its loads. That is
+// 1.5 times the bytes per flop of a 256-row tile (MT = 8, the whole AGPR file,
+// one workgroup per CU), and measured faster: prefill step 1.6 % (gate/up
+// 387 -> 382 us, down 219 -> 213 us), 4096-token TP shard 2.2 % (199 -> 194
+// us against 256-row tiles with A by direct-to-LDS loads), two A/B pairs on
+// one box each. The router's split-K product uses MT = 4 at one workgroup per
+// CU.
 //
 // Operand paths. A wave's weight fragments are private to it and come straight
 // from global memory into registers (buffer loads: the row block's base in a
@@ -31,15 +36,6 @@
 // move. (The two halves of a segment go to two stage buffers that map to the
 // same banks, a two-way conflict on those writes; a mapping without it
 // measured no faster.)
-//
-// The dense TP shard (one group, A re-read from the L2 by every n-tile) moves
-// A instead straight from global memory into LDS (global_load_lds_dwordx4,
-// one 1 KB lane-linear block per wave instruction): each lane fetches the
-// 16-byte chunk that the XOR swizzle of 128-byte stage-pair rows puts at its
-// position, one direct load per MFMA pair of each even stage's first k-step,
-// and the waits on them are counted by hand (below). Measured 4 % faster on
-// the 4096-token shard (199.6 vs 207.8 us) and level or slower on the grouped
-// GEMMs, whose A chunks are read fewer times.
 //
 // Pipeline. BK = 32 per stage (two MFMA k-steps). Weight fragments are loaded
 // three stages ahead into four register slots that rotate through a K loop
@@ -117,30 +113,6 @@ struct GemmParams {
 // row) is a permutation of the row's chunks, conflict-free either way.
 __device__ __forceinline__ int swz(int r, int chunk) {
   return r * ROWB + ((chunk ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
-}
-
-// end of an odd stage (or of a tile's prologue): this wave's loads of the
-// next stage pair have landed (only the N weight loads issued since may still
-// be pending), then the barrier publishes the pair to every wave
-// (a bare s_barrier: a fence would wait for every pending load, the weights
-// included, since the direct loads are LDS writes in flight)
-template <int N>
-__device__ __forceinline__ void vm_wait() {  // at most N vector-memory loads pending
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-  __builtin_amdgcn_sched_barrier(0);
-}
-template <int N>
-__device__ __forceinline__ void pair_ready() {
-  vm_wait<N>();
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-constexpr int PAIRB = 2 * ROWB;  // bytes of one A row of a stage pair (128)
-// chunk c (0..7) of pair row r at physical chunk c ^ g(r), g(r) = (r ^ (r >> 3)) % 8
-__device__ __forceinline__ int swz2(int r, int chunk) {
-  return r * PAIRB + ((chunk ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& w, const u32x4& a, const f32x16& c) {
@@ -299,168 +271,11 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MT][2], const char* abase,
 #undef MF_GEMM_STEP
 }
 
-template <int MT, int NM, bool TAIL, bool ROT>
-__device__ __forceinline__ void k_loop_dtl(f32x16 (&acc)[MT][2], const char* abase,
-                                           const int (&arow)[MT], int64_t Kb,
-                                           const char* const (&bp)[2],
-                                           char (&lds0)[MT * 32 * PAIRB],
-                                           char (&lds1)[MT * 32 * PAIRB], int nk, int ld_r,
-                                           int ld_c, int wave, int lane, int rot) {
-  u32x4 breg[SLOTS][4];
-  const int lr = lane & 31, lg = lane >> 5;
-  auto rotk = [&](int kt) {
-    if constexpr (ROT) {
-      const int r = kt + rot;
-      return r >= nk ? r - nk : r;
-    } else {
-      return kt;
-    }
-  };
-  // A stage pair straight into LDS: one 16-byte load per lane and live
-  // sub-tile; instruction i of wave w fills rows 32 i + 8 w .. +7 of the pair
-  // buffer (1 KB, lane-linear), lane l taking physical chunk l % 8 of row
-  // 32 i + ld_r, i.e. logical chunk (l % 8) ^ g(row) of the row's 128 bytes.
-  const int g0 = (ld_r & 7) ^ (ld_r >> 3);
-  const char* asrc[NM];
-#pragma unroll
-  for (int i = 0; i < NM; ++i)
-    asrc[i] = abase + static_cast<int64_t>(arow[i]) * Kb + (((ld_c ^ g0 ^ ((i & 1) << 2))) << 4);
-  auto dtl_pair = [&](int kt, int pb) {  // stages kt, kt + 1 (kt even) into pair buffer pb
-    const int64_t ka = static_cast<int64_t>(rotk(kt)) * ROWB;
-#pragma unroll
-    for (int i = 0; i < NM; ++i)
-      __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(asrc[i] + ka),
-          (__attribute__((address_space(3))) void*)((pb ? lds1 : lds0) + (i * 32 + wave * 8) * PAIRB),
-          16, 0, 0);
-  };
-  __amdgpu_buffer_rsrc_t wrs[2];
-#pragma unroll
-  for (int jn = 0; jn < 2; ++jn) wrs[jn] = wave_rsrc(bp[jn] - lane * 16);
-  auto load_b = [&](u32x4 (&br)[4], int kt) {
-    const int kb = rotk(kt) * (2 * FRAG);
-#pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) br[jn * 2 + s] = ld16_buf(wrs[jn], lane * 16 + kb + s * FRAG);
-  };
-  // stage t = pair buffer pb, member j (compile-time constants at every call)
-  auto stage = [&](const u32x4 (&br)[4], int t, int pb, int j, u32x4 (&b_dst)[4], int kt_b) {
-    const char* rb = pb ? lds1 : lds0;
-    u32x4 af[2][NM];
-    if (j == 0) {
-      // k-step 0 with the pair's direct loads spread between its MFMAs (one
-      // per MFMA pair), then k-step 1 with the weight loads spread the same
-      // way: the pair is issued before the stage's weights, as the waits
-      // assume. The last even stage re-loads the final pair into the idle
-      // buffer (branch-free; the tile's closing barrier waits for it).
-      const int kp = min(t + 2, nk - 2);
-      const int64_t ka = static_cast<int64_t>(rotk(kp)) * ROWB;
-#pragma unroll
-      for (int i = 0; i < NM; ++i) af[0][i] = ld16(rb + swz2(i * 32 + lr, lg));
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        acc[i][0] = mfma32(br[0], af[0][i], acc[i][0]);
-        acc[i][1] = mfma32(br[2], af[0][i], acc[i][1]);
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void*>(asrc[i] + ka),
-            (__attribute__((address_space(3))) void*)((pb ? lds0 : lds1) + (i * 32 + wave * 8) * PAIRB),
-            16, 0, 0);
-        af[1][i] = ld16(rb + swz2(i * 32 + lr, 2 + lg));
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(b_dst, kt_b);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        acc[i][0] = mfma32(br[1], af[1][i], acc[i][0]);
-        acc[i][1] = mfma32(br[3], af[1][i], acc[i][1]);
-      }
-      constexpr int NL = 4, LO = NL > NM ? NL - NM : 0;
-      __builtin_amdgcn_sched_group_barrier(0x020, LO, 1);
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-        if (i < NL - LO) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-      }
-      return;
-    }
-    // odd stage: its weights were loaded three stages ago; since then two
-    // stages of weights (8 loads) and one pair (NM direct loads) were issued
-    // (the compiler does not count across the direct loads and would wait
-    // for every load here)
-    vm_wait<8 + NM>();
-    load_b(b_dst, kt_b);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < NM; ++i) af[s][i] = ld16(rb + swz2(i * 32 + lr, 4 + 2 * s + lg));
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        acc[i][0] = mfma32(br[s], af[s][i], acc[i][0]);
-        acc[i][1] = mfma32(br[2 + s], af[s][i], acc[i][1]);
-      }
-    // masks: MFMA 0x008, VMEM read 0x020, DS read 0x100
-    constexpr int NL = 4, LO = NL > NM ? NL - NM : 0;
-    __builtin_amdgcn_sched_group_barrier(0x020, LO, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, NM, 0);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < NL - LO) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);
-  };
-  // end of an odd stage: this wave's loads of the next pair have landed (the
-  // eight weight loads of the two stages since are all that may be pending),
-  // then the barrier publishes the pair to every wave
-
-  dtl_pair(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < PREF; ++s) load_b(breg[s], s < nk ? s : nk - 1);
-  pair_ready<4 * (PREF - 1)>();  // the pair and stage 0's weights have landed
-#define MF_GEMM_STEP(S)                                                                    \
-  {                                                                                        \
-    const int t_ = kt + (S);                                                               \
-    stage(breg[(S)], t_, ((S) >> 1) & 1, (S) & 1, breg[((S) + PREF) % SLOTS],               \
-          min(t_ + PREF, nk - 1));                                                         \
-    if ((S) & 1) pair_ready<8>();                                                          \
-  }
-  int kt = 0;
-  for (; TAIL ? kt + SLOTS <= nk : kt < nk; kt += SLOTS) {
-    MF_GEMM_STEP(0)
-    MF_GEMM_STEP(1)
-    MF_GEMM_STEP(2)
-    MF_GEMM_STEP(3)
-  }
-  if constexpr (TAIL) {
-    MF_GEMM_STEP(0)
-    MF_GEMM_STEP(1)
-  }
-#undef MF_GEMM_STEP
-}
-
-template <int MT, bool GATED, bool OUT_F32, bool TAIL, bool DTL>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int BM = MT * 32;
+template <int MT, bool GATED, bool OUT_F32, bool TAIL, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(MT == 4, "128-row tiles");
   constexpr int BN_OUT = GATED ? 128 : 256;
-  // A staging: four stage buffers (register path), or two stage-pair buffers
-  // as separate objects (direct path, so that the compiler can tell a read
-  // of one from a pending direct load into the other); the other path's
-  // arrays shrink to a token size
-  __shared__ __attribute__((aligned(16))) char lds[4][DTL ? 16 : BM * ROWB];
-  __shared__ __attribute__((aligned(16))) char lds0[DTL ? BM * PAIRB : 16];
-  __shared__ __attribute__((aligned(16))) char lds1[DTL ? BM * PAIRB : 16];
+  __shared__ __attribute__((aligned(16))) char lds[4][MT * 32 * ROWB];  // A stage buffers
   __shared__ int s_tile0[MAX_GROUPS + 1];
   __shared__ int s_beg[MAX_GROUPS];
   __shared__ int s_end[MAX_GROUPS];
@@ -514,26 +329,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
   const int64_t kofs_b = static_cast<int64_t>(blockIdx.y) * (p.kc / 16) * FRAG;
   char* const cbase = p.c + static_cast<int64_t>(blockIdx.y) * p.c_split * (OUT_F32 ? 4 : 2);
 
-  // Split tail. The tiles past the last full round of G would leave the other
-  // workgroups idle for a whole tile time (prefill gate/up: 896 tiles on 256
-  // workgroups, busy 277-413 us against a 413 us launch). When that round is
-  // at most half full, each of its tiles runs as two units, each with half of
-  // the chunk's sub-tiles over the whole contraction: no partial sums to
-  // exchange, every output row written by one workgroup, the same arithmetic.
-  const int full_t = (total_tiles / G) * G;
-  const int tail_t = total_tiles - full_t;
-  const bool split = MT == 8 && tail_t > 0 && 2 * tail_t <= G;
-  const int total_units = split ? full_t + 2 * tail_t : total_tiles;
-
   for (int it = 0;; it += G) {
-    const int U = it + xcd * (G >> 3) + slot;
-    if (U >= total_units) break;
-    // tile L; for a split tail tile, its first (half 0) or second row half
-    int L = U, half = -1;
-    if (split && U >= full_t) {
-      L = full_t + ((U - full_t) >> 1);
-      half = (U - full_t) & 1;
-    }
+    const int L = it + xcd * (G >> 3) + slot;
+    if (L >= total_tiles) break;
 
     // group e: the last with s_tile0[e] <= L (it owns tile L)
     int lo = 0, hi = p.e_count - 1;
@@ -548,12 +346,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     const int ni = t / nch, mi = t - ni * nch;  // n-tile major, chunk minor
     const int q = sub_e / nch, r = sub_e - q * nch;
     const int zc = mi * q + min(mi, r);            // first sub-tile of the chunk
-    const int nmc = q + (mi < r ? 1 : 0);          // sub-tiles in the chunk
-    // a split tail tile: the first ceil(nmc/2) sub-tiles, or the rest
-    const int z0 = half > 0 ? zc + (nmc + 1) / 2 : zc;
-    const int nm = half < 0 ? nmc : (half == 0 ? (nmc + 1) / 2 : nmc / 2);
-    if (nm == 0) continue;  // the second half of a one-sub-tile chunk
-    const int row0 = s_beg[e] + z0 * 32;
+    const int nm = q + (mi < r ? 1 : 0);           // sub-tiles in the chunk
+    const int row0 = s_beg[e] + zc * 32;
     const int rows_valid = min(nm * 32, s_end[e] - row0);
     const int n0 = ni * BN_OUT;
 
@@ -568,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
       if (p.a_rows != nullptr) ar = clampi(p.a_rows[ar], 0, p.a_src_rows - 1);
       arow[i] = ar;
     }
-    const char* abase = p.a + kofs_a + (DTL ? 0 : ld_c * 16);
+    const char* abase = p.a + kofs_a + ld_c * 16;
     const char* bp[2];
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn) {
@@ -591,37 +385,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
     // stage 48.2 -> 44.2 us at 8192 tokens. The grouped GEMMs keep the common
     // start: there, tiles sharing a weight n-tile or an A chunk read it from
     // the L2 together, and rotated starts measured 12-14 % slower.
-    const int rot = MT == 4 ? 2 * ((L * 7) % (nk / 2)) : 0;
+    constexpr bool ROT = MT == 4 && OUT_F32 && OCC == 1;  // the router only
+    const int rot = ROT ? 2 * ((L * 7) % (nk / 2)) : 0;
     __syncthreads();  // the previous tile's LDS reads are done
-#define MF_K_LOOP(NMC)                                                                       \
-  if constexpr (DTL) {                                                                     \
-    static_assert(MT == 8, "the direct path is built for 256-row tiles");                 \
-    k_loop_dtl<MT, NMC, TAIL, false>(acc, abase, arow, Kb, bp, lds0, lds1, nk, ld_r, ld_c, \
-                                     wave, lane, rot);                                     \
-  } else {                                                                                 \
-    k_loop<MT, NMC, TAIL, MT == 4>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane, rot); \
-  }
-    if constexpr (MT == 8) {
-      switch (nm) {
-        case 1: MF_K_LOOP(1) break;
-        case 2: MF_K_LOOP(2) break;
-        case 3: MF_K_LOOP(3) break;
-        case 4: MF_K_LOOP(4) break;
-        case 5: MF_K_LOOP(5) break;
-        case 6: MF_K_LOOP(6) break;
-        case 7: MF_K_LOOP(7) break;
-        default: MF_K_LOOP(8) break;
-      }
-    } else {
-      static_assert(MT == 4, "MT is 4 or 8");
-      switch (nm) {
-        case 1: MF_K_LOOP(1) break;
-        case 2: MF_K_LOOP(2) break;
-        case 3: MF_K_LOOP(3) break;
-        default: MF_K_LOOP(4) break;
-      }
+    switch (nm) {  // a K loop instantiated for the tile's live sub-tiles
+      case 1: k_loop<MT, 1, TAIL, ROT>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane, rot); break;
+      case 2: k_loop<MT, 2, TAIL, ROT>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane, rot); break;
+      case 3: k_loop<MT, 3, TAIL, ROT>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane, rot); break;
+      default: k_loop<MT, 4, TAIL, ROT>(acc, abase, arow, Kb, bp, lds, nk, ld_r, ld_c, lane, rot); break;
     }
-#undef MF_K_LOOP
 
     // ---- epilogue ----------------------------------------------------------
     // Lane l holds, for row lr of sub-tile i, output columns
@@ -677,8 +449,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmParams p) {
 
 namespace {
 
-constexpr int MT_GROUPED = 8;  // 256-row tiles for the grouped and dense GEMMs
-constexpr int MT_SPLITK = 4;   // 128-row tiles for the router's split-K product
+constexpr int MT_SPLITK = 4;  // 128-row tiles for the router's split-K product
+constexpr int MT_PAIR = 4;    // the grouped and dense GEMMs: 128-row tiles, two per CU
 
 // A contraction of K % 128 == 64 (a multiple of 64 but not of the four-stage
 // loop body) takes the kernels with the two-stage tail.
@@ -707,19 +479,13 @@ void launch_gemm_gateup_bf16(const void* a, const int32_t* a_rows, int64_t a_src
                static_cast<const char*>(w_gate),
                static_cast<const char*>(w_up), static_cast<char*>(h), offsets, e_count,
                static_cast<int>(max_rows), K, N / 32, N, N, K, 0, counts, cap};
-  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
+  // 128-row tiles, two workgroups per CU (two waves per SIMD); one dense
+  // group (the TP shard) when there are neither offsets nor counts
+  const int grid = persistent_grid(max_rows, MT_PAIR * 32, e_count,
                                    offsets == nullptr && counts == nullptr, (N + 127) / 128,
-                                   num_cus);
-  // one dense group (the TP shard): A through the direct path
-  const bool dense = offsets == nullptr && counts == nullptr;
-  const bool tail = tail_stages(K);
-  if (dense) {
-    if (tail) gemm_bf16_kernel<MT_GROUPED, true, false, true, true><<<grid, 256, 0, s>>>(p);
-    else gemm_bf16_kernel<MT_GROUPED, true, false, false, true><<<grid, 256, 0, s>>>(p);
-  } else {
-    if (tail) gemm_bf16_kernel<MT_GROUPED, true, false, true, false><<<grid, 256, 0, s>>>(p);
-    else gemm_bf16_kernel<MT_GROUPED, true, false, false, false><<<grid, 256, 0, s>>>(p);
-  }
+                                   2 * num_cus);
+  if (tail_stages(K)) gemm_bf16_kernel<MT_PAIR, true, false, true, 2><<<grid, 256, 0, s>>>(p);
+  else gemm_bf16_kernel<MT_PAIR, true, false, false, 2><<<grid, 256, 0, s>>>(p);
 }
 
 void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, int64_t max_rows,
@@ -728,17 +494,16 @@ void launch_gemm_down_bf16(const void* a, const int32_t* offsets, int e_count, i
   GemmParams p{static_cast<const char*>(a), nullptr, 0, static_cast<const char*>(w_down), nullptr,
                static_cast<char*>(y), offsets, e_count, static_cast<int>(max_rows), K, N / 32,
                N, N, K, 0, counts, cap};
-  const int grid = persistent_grid(max_rows, MT_GROUPED * 32, e_count,
+  const int grid = persistent_grid(max_rows, MT_PAIR * 32, e_count,
                                    offsets == nullptr && counts == nullptr, (N + 255) / 256,
-                                   num_cus);
+                                   2 * num_cus);
   const bool tail = tail_stages(K);
-  // the fp32 output is the TP shard's partial sum: A through the direct path
-  if (out_f32) {
-    if (tail) gemm_bf16_kernel<MT_GROUPED, false, true, true, true><<<grid, 256, 0, s>>>(p);
-    else gemm_bf16_kernel<MT_GROUPED, false, true, false, true><<<grid, 256, 0, s>>>(p);
+  if (out_f32) {  // the TP shard's fp32 partial sum
+    if (tail) gemm_bf16_kernel<MT_PAIR, false, true, true, 2><<<grid, 256, 0, s>>>(p);
+    else gemm_bf16_kernel<MT_PAIR, false, true, false, 2><<<grid, 256, 0, s>>>(p);
   } else {
-    if (tail) gemm_bf16_kernel<MT_GROUPED, false, false, true, false><<<grid, 256, 0, s>>>(p);
-    else gemm_bf16_kernel<MT_GROUPED, false, false, false, false><<<grid, 256, 0, s>>>(p);
+    if (tail) gemm_bf16_kernel<MT_PAIR, false, false, true, 2><<<grid, 256, 0, s>>>(p);
+    else gemm_bf16_kernel<MT_PAIR, false, false, false, 2><<<grid, 256, 0, s>>>(p);
   }
 }
 
@@ -754,9 +519,9 @@ void launch_gemm_nt_f32_splitk(const void* a, int64_t rows, int K, const void* b
   // splits x tiles workgroups: size x so that all of them fit in one round
   int gx = persistent_grid(rows, MT_SPLITK * 32, 1, true, 1, num_cus / splits);
   if (tail_stages(K / splits))
-    gemm_bf16_kernel<MT_SPLITK, false, true, true, false><<<dim3(gx, splits), 256, 0, s>>>(p);
+    gemm_bf16_kernel<MT_SPLITK, false, true, true, 1><<<dim3(gx, splits), 256, 0, s>>>(p);
   else
-    gemm_bf16_kernel<MT_SPLITK, false, true, false, false><<<dim3(gx, splits), 256, 0, s>>>(p);
+    gemm_bf16_kernel<MT_SPLITK, false, true, false, 1><<<dim3(gx, splits), 256, 0, s>>>(p);
 }
 
 }  // namespace mf
